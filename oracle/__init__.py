@@ -1,0 +1,27 @@
+"""CPU oracle for the DeepSeekMoE-style MoE FFN layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or run
+anything in this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+path (``fine_grained_routed_amd``); the two meet only in the input bytes drawn
+by ``workloads``.
+"""
+from .moe_oracle import (  # noqa: F401
+    router_logits,
+    exact_logit,
+    route,
+    softmax,
+    permute,
+    silu,
+    swiglu,
+    expert_ffn,
+    combine,
+    forward,
+    forward_dense,
+)
+from .accounting import (  # noqa: F401
+    combinations,
+    expert_budget,
+    layer_accounting,
+    granularity_rows,
+)

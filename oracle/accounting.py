@@ -1,0 +1,98 @@
+"""Parameter and combination accounting for fine-grained and shared experts.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Every function restates a counting rule from the pages in plain integer
+arithmetic.  Nothing here is used by the HIP path.
+"""
+from __future__ import annotations
+
+from typing import List, Tuple
+
+
+def combinations(n_experts: int, top_k: int) -> int:
+    """Number of distinct expert sets a top-k router can pick from n experts.
+
+    "Shared and fine-grained experts", Researcher level, "Why segmentation
+    helps": the reachable function class is indexed by the selected set, so its
+    size is the binomial coefficient C(N, K); segmentation by m turns it into
+    C(mN, mK).  Computed here as the product formula over exact integers.
+    """
+    if top_k < 0 or top_k > n_experts:
+        return 0
+    k = min(top_k, n_experts - top_k)
+    num = 1
+    den = 1
+    for i in range(k):
+        num *= n_experts - i
+        den *= i + 1
+    assert num % den == 0
+    return num // den
+
+
+def expert_budget(width: int, intermediate: int, routed: int, top_k: int, shared: int = 0) -> Tuple[int, int]:
+    """(total, active) expert weights of one MoE layer, biases ignored.
+
+    Chinese page on fine-grained and shared experts, section on making the
+    budget equal: a SwiGLU expert holds three d x f matrices (gate, up, down),
+    i.e. 3*d*f weights and as many MACs per token; the shared experts count in
+    both the stored and the active totals.  Invalid configurations are
+    rejected.
+    """
+    if min(width, intermediate, routed, top_k) < 1 or shared < 0 or top_k > routed:
+        raise ValueError("invalid expert configuration")
+    per_expert = 3 * width * intermediate
+    return per_expert * (routed + shared), per_expert * (top_k + shared)
+
+
+def layer_accounting(d_model: int, d_ff: int, n_routed: int, n_shared: int, top_k: int) -> dict:
+    """Per-layer parameter accounting of a shared + routed MoE layer.
+
+    "Shared and fine-grained experts", Developer level, DeepSeek-V3 accounting:
+    each expert has gate, up and down projections (3*d*f); the layer stores all
+    routed and shared experts plus the router (d weights per routed expert);
+    a token activates its top-k routed experts, the shared experts and the
+    whole router.
+    """
+    per_expert = 3 * d_model * d_ff
+    router = d_model * n_routed
+    total = (n_routed + n_shared) * per_expert + router
+    active = (top_k + n_shared) * per_expert + router
+    return {
+        "per_expert": per_expert,
+        "router": router,
+        "total": total,
+        "active": active,
+        "active_fraction": active / total,
+        "shared_params": n_shared * per_expert,
+        # share of the active feed-forward work done by the shared experts
+        "shared_share": n_shared / (top_k + n_shared),
+    }
+
+
+def granularity_rows(base_ff: int, n0: int, k0: int, ms: List[int]) -> List[dict]:
+    """Fine-grained segmentation at constant compute per token.
+
+    "Shared and fine-grained experts", Developer level, counting the
+    combinations: splitting by m multiplies the expert count and top-k by m and
+    divides the expert width by m (integer division), so the active width
+    k*f stays fixed while the number of combinations grows.
+    """
+    rows = []
+    for m in ms:
+        n, k = n0 * m, k0 * m
+        ff = base_ff // m
+        rows.append({"m": m, "experts": n, "top_k": k, "expert_ff": ff,
+                     "active_ff": k * ff, "combinations": combinations(n, k)})
+    return rows
+
+
+def sparsity(n_experts: int, top_k: int) -> float:
+    """Fraction of routed experts active per token ("Expert Count Selection")."""
+    return top_k / n_experts
+
+
+def capacity_to_compute(n_experts: int, top_k: int) -> float:
+    """Routed parameters held per routed parameter used ("Expert Count Selection")."""
+    return n_experts / top_k
+
