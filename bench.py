@@ -1,0 +1,188 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE-layer forward tokens/s at the DeepSeek-V3 shape on one MI355X.
+
+One step = one moe_layer_forward (router, top-k, permutation, grouped gate/up,
+grouped down, combine) over T tokens already resident in HBM.  Prints ONE JSON
+line.  Per-stage times come from HIP events the library records on the launch
+stream; the roofline block reports the dominant kernel (grouped gate/up GEMM)
+against the bf16 dense matrix-core peak.  A decode-size measurement (T = 64,
+same weights) reports achieved HBM bandwidth over the touched experts'
+weights.  The CPU oracle is timed on a bounded token slice as a baseline.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12  # 2516.6: 256 CUs x 4096 FLOP/clk x 2.4 GHz (dense)
+PEAK_HBM_GBS = 8000.0
+STAGES = ["router_logits", "topk", "permute", "gate_up", "down", "combine"]
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            evs.append(e.value)
+        return evs
+
+    def ms(self, a, b) -> float:
+        out = ctypes.c_float()
+        self.hip.hipEventSynchronize(b)
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return out.value
+
+
+def timed_steps(layer, u, steps, warmup, path, hev):
+    import torch
+    for _ in range(warmup):
+        layer.forward(u, path=path)
+    evs = [hev.create(7) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        layer.forward(u, path=path, events=evs[s])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    stage = {name: sum(hev.ms(e[i], e[i + 1]) for e in evs) / steps for i, name in enumerate(STAGES)}
+    total = sum(hev.ms(e[0], e[6]) for e in evs) / steps
+    return wall_ms, total, stage
+
+
+def cpu_baseline(wl, inp, n_tokens):
+    """The oracle as it stands, on the first n_tokens tokens (weights staged on the host, untimed)."""
+    import torch
+    import numpy as np
+    import oracle
+    import workloads
+    host = {k: (None if v is None else v.to("cpu")) for k, v in inp.items()}
+    u64 = host["u"][:n_tokens].to(torch.float64).numpy()
+    args = dict(w_router=workloads.to_f64(host["w_router"]), w1=workloads.F64Experts(host["w1"]),
+                w3=workloads.F64Experts(host["w3"]), w2=workloads.F64Experts(host["w2"]), k=wl.top_k,
+                bias=workloads.to_f64(host["router_bias"]), w1s=workloads.to_f64(host["w1s"]),
+                w3s=workloads.to_f64(host["w3s"]), w2s=workloads.to_f64(host["w2s"]))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
+    except Exception:
+        blas = 1
+    cores = max(blas, torch.get_num_threads())
+    t0 = time.perf_counter()
+    oracle.forward(u64, **args)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_tokens} tokens of {wl.name}; fp64 numpy oracle incl. per-expert widening of "
+                      f"host bf16 weights to fp64; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the layer runs on a single MI355X; see the sharding notes in the design document)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    from fine_grained_routed_amd import PATH_AUTO, PATH_DECODE, MoELayer
+
+    torch.cuda.set_device(0)
+    wl = workloads.get(args.workload)
+    print(f"[bench] drawing inputs for {wl.name}", file=sys.stderr, flush=True)
+    inp = workloads.make_inputs(wl, seed=args.seed, device="cuda")
+    layer = MoELayer({k: v for k, v in inp.items() if k != "u"}, wl.top_k)
+    hev = HipEvents()
+    u = inp["u"]
+    T = u.shape[0]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    wall_ms, ev_ms, stage = timed_steps(layer, u, args.steps, args.warmup, PATH_AUTO, hev)
+
+    R = T * wl.top_k
+    gu_flop = 4.0 * wl.d * (R * wl.d_ff + T * wl.d_ff_shared)
+    dn_flop = gu_flop / 2.0
+    total_flop = wl.flops(T)
+    gu_tflops = gu_flop / (stage["gate_up"] * 1e-3) / 1e12
+    result = {
+        "metric": "MoE-layer tokens/s at DeepSeek-V3 shape; % bf16 MFMA peak (prefill), % HBM (decode)",
+        "value": T / (wall_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded RMS-normalised N(0,1) tokens, N(0,0.02) weights",
+        "config": {"workload": wl.name, "T": T, "d_model": wl.d, "n_routed": wl.n_routed, "d_ff": wl.d_ff,
+                   "n_shared": wl.n_shared, "top_k": wl.top_k},
+        "roofline": {"bound": "mfma", "kernel": "grouped_gemm_bf16_kernel<gate_up>",
+                     "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gu_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+        "layer_tflops": total_flop / (wall_ms * 1e-3) / 1e12,
+        "layer_frac_of_peak": total_flop / (wall_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "stage_ms": stage,
+        "event_ms_per_step": ev_ms,
+        "down_tflops": dn_flop / (stage["down"] * 1e-3) / 1e12,
+    }
+
+    if not args.no_decode and wl.name == "dsv3_prefill":
+        dec = workloads.get("dsv3_decode")
+        ud = u[:dec.T].contiguous()
+        d_wall, d_ev, d_stage = timed_steps(layer, ud, max(args.steps, 20), args.warmup, PATH_DECODE, hev)
+        idx, _ = layer.router_topk(ud)
+        counts = layer.permute(idx)[0].cpu()
+        touched = int((counts > 0).sum())
+        eb = 2  # bf16
+        gu_bytes = eb * (touched * 2 * wl.d_ff * wl.d + 2 * wl.d_ff_shared * wl.d)
+        dn_bytes = eb * (touched * wl.d * wl.d_ff + wl.d * wl.d_ff_shared)
+        layer_bytes = gu_bytes + dn_bytes + eb * (wl.n_routed * wl.d + dec.T * wl.d) + 4 * dec.T * wl.d
+        result["decode"] = {
+            "workload": dec.name, "T": dec.T, "tokens_per_s": dec.T / (d_wall * 1e-3), "ms_per_step": d_wall,
+            "touched_experts": touched, "stage_ms": d_stage,
+            "layer_GBps": layer_bytes / (d_wall * 1e-3) / 1e9,
+            "layer_frac_hbm": layer_bytes / (d_wall * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "roofline": {"bound": "hbm", "kernel": "gate_up (decode path)",
+                         "achieved": gu_bytes / (d_stage["gate_up"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": gu_bytes / (d_stage["gate_up"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "traffic": None},
+        }
+
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the oracle on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

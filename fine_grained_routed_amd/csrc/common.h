@@ -1,0 +1,168 @@
+// Device and host helpers shared by the library's HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+#define MOE_WAVE 64
+
+// ----------------------------------------------------------------- bf16 helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
+  union { uint4 u; bf16x8_t b; } c;
+  c.u = v;
+  return c.b;
+}
+
+// 16-byte load that bypasses cache retention (streamed data read once)
+__device__ __forceinline__ uint4 load_stream16(const void *p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// keep v when ok, else zeros (component-wise, so it stays in registers)
+__device__ __forceinline__ uint4 keep_or_zero(bool ok, uint4 v) {
+  const uint32_t m = ok ? 0xffffffffu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+// ------------------------------------------------------------ wave reductions
+__device__ __forceinline__ double wave_max_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ long long wave_sum_i64(long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------- workspace layout
+// The diagnostics header sits at offset 0 of every workspace.
+#define MOE_DIAG_UNRESOLVED 1u
+#define MOE_DIAG_BAD_INDEX 2u
+#define MOE_DIAG_DUPLICATE 4u
+
+struct DiagWords {
+  uint32_t flags;
+  uint32_t tokens_exact;
+  uint32_t exact_keys;
+  uint32_t refinements;
+};
+
+// M-tile heights for which the permutation writes per-expert tile prefixes.
+#define MOE_N_BM 5
+__host__ __device__ constexpr int moe_bm_of(int i) { return 16 << i; }  // 16 32 64 128 256
+
+// Routing block: tokens per permutation work-group.
+#define MOE_PERM_BLOCK 256
+
+struct WsLayout {
+  size_t diag;        // DiagWords
+  size_t logits;      // double [T, N_r]
+  size_t unorm2;      // double [T]   squared 2-norm of each token row
+  size_t wnorm2;      // double [N_r] squared 2-norm of each router row
+  size_t blk;         // int32  [nblk, N_r] per-block histograms, then bases
+  size_t tile_off;    // int32  [MOE_N_BM, N_r + 2] per-expert m-tile prefixes (+ shared)
+  size_t h;           // bf16 or f32 [R, f] routed hidden activations
+  size_t h_sh;        // bf16 or f32 [T, f_s] shared hidden activations
+  size_t topk_idx;    // int32 [T, k]  (layer forward only)
+  size_t topk_w;      // f32   [T, k]
+  size_t counts;      // int32 [N_r]
+  size_t offsets;     // int32 [N_r + 1]
+  size_t row_token;   // int32 [R]
+  size_t token_row;   // int32 [T, k]
+  size_t y_rows;      // f32 [R, d]
+  size_t y_sh;        // f32 [T, d]
+  size_t total;
+};
+
+static inline size_t moe_align(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static inline WsLayout moe_ws_layout(const moe_dims &dm, int64_t T) {
+  WsLayout L;
+  const size_t E = (size_t)dm.n_routed, k = (size_t)dm.top_k, d = (size_t)dm.d_model;
+  const size_t R = (size_t)T * k, f = (size_t)dm.d_ff, fs = (size_t)dm.d_ff_shared;
+  const size_t hbytes = dm.dtype == MOE_BF16 ? 2 : 4;
+  const size_t nblk = ((size_t)T + MOE_PERM_BLOCK - 1) / MOE_PERM_BLOCK;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = moe_align(o + bytes); return at; };
+  L.diag = take(256);
+  L.logits = take((size_t)T * E * 8);
+  L.unorm2 = take((size_t)T * 8);
+  L.wnorm2 = take(E * 8);
+  L.blk = take(nblk * E * 4);
+  L.tile_off = take((size_t)MOE_N_BM * (E + 2) * 4);
+  L.h = take(R * f * hbytes);
+  L.h_sh = take((size_t)T * fs * hbytes);
+  L.topk_idx = take(R * 4);
+  L.topk_w = take(R * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.row_token = take(R * 4);
+  L.token_row = take(R * 4);
+  L.y_rows = take(R * d * 4);
+  L.y_sh = take((size_t)T * d * 4);
+  L.total = o;
+  return L;
+}
+
+// ------------------------------------------------------ kernel launch wrappers
+// Implemented in the per-stage sources; all enqueue on `st` and return the
+// launch status.
+hipError_t launch_diag_clear(void *ws, hipStream_t st);
+hipError_t launch_router_logits(const moe_dims &dm, int64_t T, const void *u, const void *w_router,
+                                const float *bias, const WsLayout &L, char *ws, hipStream_t st);
+hipError_t launch_topk(const moe_dims &dm, int64_t T, const void *u, const void *w_router, const float *bias,
+                       int32_t *topk_idx, float *topk_w, const WsLayout &L, char *ws, hipStream_t st);
+hipError_t launch_permute(const moe_dims &dm, int64_t T, const int32_t *topk_idx, int32_t *counts,
+                          int32_t *offsets, int32_t *row_token, int32_t *token_row, const WsLayout &L,
+                          char *ws, hipStream_t st);
+hipError_t launch_tile_offsets(const moe_dims &dm, int64_t T, const int32_t *counts, const WsLayout &L,
+                               char *ws, hipStream_t st);
+hipError_t launch_ffn_prefill(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w,
+                              const int32_t *offsets, const int32_t *row_token, float *y_rows, float *y_sh,
+                              const WsLayout &L, char *ws, hipStream_t st, hipEvent_t ev_mid);
+hipError_t launch_ffn_decode(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w,
+                             const int32_t *counts, const int32_t *offsets, const int32_t *row_token,
+                             float *y_rows, float *y_sh, const WsLayout &L, char *ws, hipStream_t st,
+                             hipEvent_t ev_mid);
+hipError_t launch_combine(const moe_dims &dm, int64_t T, const float *y_rows, const float *y_sh,
+                          const float *topk_w, const int32_t *token_row, void *out, hipStream_t st);

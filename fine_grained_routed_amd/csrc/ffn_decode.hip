@@ -1,0 +1,224 @@
+// Decode path: expert FFNs for small token counts as HBM weight streaming.
+//
+// Source: "Shared and fine-grained experts", Developer level, 'Why not go finer
+// still': an expert processing a handful of tokens is a tiny GEMM that is
+// bound by loading its weights; Researcher level, Systems limits: grouped
+// kernels over many small experts.  "Shared Expert" (How it works): the
+// shared MLP runs on every token; here it is one more group.
+//
+// Work items are (16-row tile, 128-column slice) pairs over the device-side
+// tile list of the permutation (16-row tiles; the shared group appended), so
+// experts that received no token have no tile and cost nothing.  Each of the
+// 4 waves of a work-group owns 32 output columns and walks the whole reduction
+// depth, loading the weight fragments of 16x16x32 matrix-core steps straight
+// from HBM into registers with non-temporal loads (no LDS: each weight
+// element is used by this wave only); the 16 token rows are re-read from L2.
+// An expert's weights are streamed once per 16 of its rows (once for nearly
+// every expert at decode sizes; the tiles of one expert run together, so
+// repeats mostly hit L2).  Loads are issued DK_UNROLL steps ahead of use.
+//
+// gate/up: H[r, n] = SiLU(A[r,:] . W1_g[n,:]) * (A[r,:] . W3_g[n,:]), bf16 out
+// down:    Y[r, n] = H[r,:] . W2_g[n,:], fp32 out
+#include <algorithm>
+
+#include "common.h"
+
+#define DK_BM 16                               // rows per tile (one MFMA row tile)
+#define DK_BM_IDX 0                            // moe_bm_of(0) == 16
+#define DK_NT 2                                // 16-column MFMA tiles per wave
+#define DK_WAVES 4
+#define DK_COLS (16 * DK_NT * DK_WAVES)        // columns per work-group
+#define DK_UNROLL 4                            // 32-deep steps per load batch
+
+struct DecodeArgs {
+  const uint16_t *A, *A_sh;      // gate/up: u [T, d] (gathered); down: H [R, f], H_sh [T, f_s]
+  const int32_t *row_token;      // gate/up routed rows -> token
+  const int32_t *offsets;        // [E + 1]
+  const int32_t *tile_off;       // [E + 2] 16-row tile prefix (shared appended)
+  const uint16_t *B1, *B3;       // routed weights [E, N, K] (B3: up, gate/up only)
+  const uint16_t *B1s, *B3s;     // shared weights [N_sh, K_sh]
+  void *C, *C_sh;                // gate/up: H / H_sh bf16; down: Y / Y_sh fp32
+  int64_t T;
+  int E, K, K_sh, N, N_sh;
+  int ns_r, ns_s;                // column slices of a routed / the shared group
+};
+
+__device__ __forceinline__ float dk_silu(float g) { return g / (1.0f + __expf(-g)); }
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // ---- tile lookup: (16-row tile, column slice), routed tiles first
+  const int mt_r = a.tile_off[a.E];
+  const int mt_s = a.tile_off[a.E + 1] - mt_r;
+  const int64_t tiles_r = (int64_t)mt_r * a.ns_r;
+  const int64_t tile = blockIdx.x;
+  if (tile >= tiles_r + (int64_t)mt_s * a.ns_s) return;
+  bool shared;
+  int g, slice, K, N, valid;
+  int64_t rb;
+  if (tile < tiles_r) {
+    shared = false;
+    const int mt = (int)(tile / a.ns_r);
+    slice = (int)(tile % a.ns_r);
+    int lo = 0, hi = a.E - 1;  // largest g with tile_off[g] <= mt
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.tile_off[mid] <= mt) lo = mid; else hi = mid - 1;
+    }
+    g = lo;
+    const int m0 = (mt - a.tile_off[g]) * DK_BM;
+    valid = min(DK_BM, a.offsets[g + 1] - a.offsets[g] - m0);
+    rb = (int64_t)a.offsets[g] + m0;
+    K = a.K;
+    N = a.N;
+  } else {
+    shared = true;
+    const int64_t ts = tile - tiles_r;
+    const int mt = (int)(ts / a.ns_s);
+    slice = (int)(ts % a.ns_s);
+    g = a.E;
+    rb = (int64_t)mt * DK_BM;
+    valid = (int)min((int64_t)DK_BM, a.T - rb);
+    K = a.K_sh;
+    N = a.N_sh;
+  }
+  const int n0 = slice * DK_COLS + wv * (16 * DK_NT);
+  if (n0 >= N) return;
+  const int kofs = (lane >> 4) * 8;  // this lane's 8-element slice of a 32-deep step
+
+  // A: this lane's row of the tile (padded rows repeat a valid row, never stored)
+  const int r = min(lane & 15, valid - 1);
+  const int64_t arow = (GATEUP && !shared) ? (int64_t)a.row_token[rb + r] : rb + r;
+  const uint16_t *ap = (shared ? a.A_sh : a.A) + arow * K + kofs;
+  // B: this lane's weight row in each of the wave's column tiles
+  const uint16_t *w1 = shared ? a.B1s : a.B1 + (int64_t)g * N * K;
+  const uint16_t *w3 = GATEUP ? (shared ? a.B3s : a.B3 + (int64_t)g * N * K) : nullptr;
+  const uint16_t *p1[DK_NT];
+  const uint16_t *p3[DK_NT];
+#pragma unroll
+  for (int j = 0; j < DK_NT; ++j) {
+    const int n = min(n0 + j * 16 + (lane & 15), N - 1);  // clamped; columns >= N are never stored
+    p1[j] = w1 + (int64_t)n * K + kofs;
+    p3[j] = GATEUP ? w3 + (int64_t)n * K + kofs : nullptr;
+  }
+  f32x4_t acc1[DK_NT], acc3[DK_NT];
+#pragma unroll
+  for (int j = 0; j < DK_NT; ++j) {
+    acc1[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc3[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // main loop: DK_UNROLL steps per batch, every load of a batch issued before
+  // the first use; remainder: single 32-deep steps
+  const int kmain = K - K % (32 * DK_UNROLL);
+  for (int k0 = 0; k0 < kmain; k0 += 32 * DK_UNROLL) {
+    uint4 av[DK_UNROLL], b1[DK_UNROLL][DK_NT], b3[DK_UNROLL][DK_NT];
+#pragma unroll
+    for (int s = 0; s < DK_UNROLL; ++s) {
+      av[s] = *(const uint4 *)(ap + k0 + 32 * s);
+#pragma unroll
+      for (int j = 0; j < DK_NT; ++j) {
+        b1[s][j] = load_stream16(p1[j] + k0 + 32 * s);
+        if (GATEUP) b3[s][j] = load_stream16(p3[j] + k0 + 32 * s);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < DK_UNROLL; ++s) {
+      const bf16x8_t a8 = as_bf16x8(av[s]);
+#pragma unroll
+      for (int j = 0; j < DK_NT; ++j) {
+        acc1[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(b1[s][j]), acc1[j], 0, 0, 0);
+        if (GATEUP) acc3[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(b3[s][j]), acc3[j], 0, 0, 0);
+      }
+    }
+  }
+  for (int k0 = kmain; k0 < K; k0 += 32) {
+    const bf16x8_t a8 = as_bf16x8(*(const uint4 *)(ap + k0));
+#pragma unroll
+    for (int j = 0; j < DK_NT; ++j) {
+      acc1[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(load_stream16(p1[j] + k0)), acc1[j], 0, 0, 0);
+      if (GATEUP)
+        acc3[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(load_stream16(p3[j] + k0)), acc3[j], 0, 0, 0);
+    }
+  }
+  // ---- epilogue: lane holds rows 4*(lane/16)+q of column lane%16 of each tile
+#pragma unroll
+  for (int j = 0; j < DK_NT; ++j) {
+    const int n = n0 + j * 16 + (lane & 15);
+    if (n >= N) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = (lane >> 4) * 4 + q;
+      if (row >= valid) continue;
+      if (GATEUP) {
+        uint16_t *C = (uint16_t *)(shared ? a.C_sh : a.C);
+        C[(rb + row) * N + n] = f32_to_bf16(dk_silu(acc1[j][q]) * acc3[j][q]);
+      } else {
+        float *C = (float *)(shared ? a.C_sh : a.C);
+        C[(rb + row) * N + n] = acc1[j][q];
+      }
+    }
+  }
+}
+
+static int64_t dk_mtile_bound(int64_t R, int E) { return (R + DK_BM - 1) / DK_BM + std::min<int64_t>(E, R); }
+
+hipError_t launch_ffn_decode(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w,
+                             const int32_t *counts, const int32_t *offsets, const int32_t *row_token,
+                             float *y_rows, float *y_sh, const WsLayout &L, char *ws, hipStream_t st,
+                             hipEvent_t ev_mid) {
+  (void)counts;
+  const int E = dm.n_routed, d = dm.d_model, f = dm.d_ff, fs = dm.d_ff_shared;
+  const int hs = fs > 0 ? 1 : 0;
+  const int64_t R = T * dm.top_k;
+  const int32_t *tile_off = (const int32_t *)(ws + L.tile_off) + DK_BM_IDX * (E + 2);
+  uint16_t *H = (uint16_t *)(ws + L.h);
+  uint16_t *Hs = (uint16_t *)(ws + L.h_sh);
+  const int64_t mt_sh = hs ? (T + DK_BM - 1) / DK_BM : 0;
+
+  DecodeArgs g1{};
+  g1.A = (const uint16_t *)u;
+  g1.A_sh = (const uint16_t *)u;
+  g1.row_token = row_token;
+  g1.offsets = offsets;
+  g1.tile_off = tile_off;
+  g1.B1 = (const uint16_t *)w.w1;
+  g1.B3 = (const uint16_t *)w.w3;
+  g1.B1s = (const uint16_t *)w.w1s;
+  g1.B3s = (const uint16_t *)w.w3s;
+  g1.C = H;
+  g1.C_sh = Hs;
+  g1.T = T;
+  g1.E = E;
+  g1.K = d;
+  g1.K_sh = d;
+  g1.N = f;
+  g1.N_sh = fs;
+  g1.ns_r = (f + DK_COLS - 1) / DK_COLS;
+  g1.ns_s = hs ? (fs + DK_COLS - 1) / DK_COLS : 1;
+  const int64_t grid1 = dk_mtile_bound(R, E) * g1.ns_r + mt_sh * g1.ns_s;
+  decode_ffn_kernel<true><<<dim3((unsigned)grid1), 256, 0, st>>>(g1);
+  if (ev_mid) (void)hipEventRecord(ev_mid, st);
+
+  DecodeArgs g2{};
+  g2.A = H;
+  g2.A_sh = Hs;
+  g2.row_token = nullptr;
+  g2.offsets = offsets;
+  g2.tile_off = tile_off;
+  g2.B1 = (const uint16_t *)w.w2;
+  g2.B1s = (const uint16_t *)w.w2s;
+  g2.C = y_rows;
+  g2.C_sh = y_sh;
+  g2.T = T;
+  g2.E = E;
+  g2.K = f;
+  g2.K_sh = fs;
+  g2.N = d;
+  g2.N_sh = d;
+  g2.ns_r = (d + DK_COLS - 1) / DK_COLS;
+  g2.ns_s = g2.ns_r;
+  const int64_t grid2 = dk_mtile_bound(R, E) * g2.ns_r + mt_sh * g2.ns_s;
+  decode_ffn_kernel<false><<<dim3((unsigned)grid2), 256, 0, st>>>(g2);
+  return hipGetLastError();
+}

@@ -1,0 +1,164 @@
+// Permutation: group the T*k (token, slot) pairs by expert, tokens ascending
+// inside each group, deterministically.
+//
+// Source: "Shared Expert" (How it works: routed expert outputs are
+// scatter-summed back to tokens); the grouping is what lets each expert run
+// as one GEMM over its tokens ("Shared and fine-grained experts", Researcher
+// level, Systems limits: grouped GEMM kernels).
+//
+// Three launches, no atomics on the global result:
+//   1. per block of 256 tokens, an LDS bitmap per expert (bit i = token i of the
+//      block chose the expert); its popcount is the block's count per expert;
+//   2. one work-group: per-expert totals, the exclusive scan over experts
+//      (offsets), and each block's starting row per expert;
+//   3. per block, rebuild the bitmap; a token's rank inside its expert group is
+//      the popcount of the bits below it, so rows follow token order.
+#include "common.h"
+
+#define PERM_WORDS (MOE_PERM_BLOCK / 64)
+
+__device__ __forceinline__ void build_bitmap(unsigned long long *bm, const int32_t *__restrict__ idx, int64_t T,
+                                             int E, int k, int64_t blk, DiagWords *diag) {
+  for (int i = threadIdx.x; i < E * PERM_WORDS; i += blockDim.x) bm[i] = 0ull;
+  __syncthreads();
+  const int i = threadIdx.x;
+  const int64_t t = blk * MOE_PERM_BLOCK + i;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[t * k + j];
+      if (e < 0 || e >= E) {
+        if (diag) atomicOr(&diag->flags, MOE_DIAG_BAD_INDEX);
+        continue;
+      }
+      const unsigned long long bit = 1ull << (i & 63);
+      const unsigned long long old = atomicOr(&bm[e * PERM_WORDS + (i >> 6)], bit);
+      if ((old & bit) && diag) atomicOr(&diag->flags, MOE_DIAG_DUPLICATE);
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(MOE_PERM_BLOCK) void perm_hist_kernel(const int32_t *__restrict__ idx, int64_t T, int E,
+                                                                   int k, int32_t *__restrict__ blk_hist,
+                                                                   DiagWords *diag) {
+  extern __shared__ unsigned long long bm[];
+  build_bitmap(bm, idx, T, E, k, blockIdx.x, diag);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < PERM_WORDS; ++q) c += __popcll(bm[e * PERM_WORDS + q]);
+    blk_hist[(int64_t)blockIdx.x * E + e] = c;
+  }
+}
+
+// Exclusive scan of v over the work-group (blockDim.x == 1024), returns the
+// exclusive prefix of this thread and writes the total to *total.
+__device__ int block_exclusive_scan(int v, int *sh, int *total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int add = tid >= o ? sh[tid - o] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  const int incl = sh[tid];
+  *total = sh[1023];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ blk_hist, int64_t nblk, int E,
+                                                         int32_t *__restrict__ counts, int32_t *__restrict__ offsets) {
+  __shared__ int sh[1024];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E) {
+    for (int64_t b = 0; b < nblk; ++b) {
+      const int c = blk_hist[b * E + e];
+      blk_hist[b * E + e] = tot;  // exclusive within the expert
+      tot += c;
+    }
+  }
+  int all;
+  const int off = block_exclusive_scan(e < E ? tot : 0, sh, &all);
+  if (e < E) {
+    counts[e] = tot;
+    offsets[e] = off;
+    for (int64_t b = 0; b < nblk; ++b) blk_hist[b * E + e] += off;
+  }
+  if (e == 0) offsets[E] = all;
+}
+
+__global__ __launch_bounds__(MOE_PERM_BLOCK) void perm_scatter_kernel(const int32_t *__restrict__ idx, int64_t T,
+                                                                      int E, int k,
+                                                                      const int32_t *__restrict__ blk_base,
+                                                                      int32_t *__restrict__ row_token,
+                                                                      int32_t *__restrict__ token_row) {
+  extern __shared__ unsigned long long bm[];
+  build_bitmap(bm, idx, T, E, k, blockIdx.x, nullptr);
+  const int i = threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * MOE_PERM_BLOCK + i;
+  if (t >= T) return;
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[t * k + j];
+    if (e < 0 || e >= E) {
+      token_row[t * k + j] = -1;
+      continue;
+    }
+    const unsigned long long *row = bm + e * PERM_WORDS;
+    int rank = 0;
+    const int w = i >> 6;
+#pragma unroll
+    for (int q = 0; q < PERM_WORDS; ++q)
+      if (q < w) rank += __popcll(row[q]);
+    const unsigned long long below = (i & 63) ? (row[w] & ((1ull << (i & 63)) - 1ull)) : 0ull;
+    rank += __popcll(below);
+    const int r = blk_base[(int64_t)blockIdx.x * E + e] + rank;
+    token_row[t * k + j] = r;
+    row_token[r] = (int32_t)t;
+  }
+}
+
+hipError_t launch_permute(const moe_dims &dm, int64_t T, const int32_t *topk_idx, int32_t *counts, int32_t *offsets,
+                          int32_t *row_token, int32_t *token_row, const WsLayout &L, char *ws, hipStream_t st) {
+  const int E = dm.n_routed, k = dm.top_k;
+  const int64_t nblk = (T + MOE_PERM_BLOCK - 1) / MOE_PERM_BLOCK;
+  int32_t *blk = (int32_t *)(ws + L.blk);
+  DiagWords *diag = (DiagWords *)(ws + L.diag);
+  const size_t lds = (size_t)E * PERM_WORDS * sizeof(unsigned long long);
+  perm_hist_kernel<<<dim3((unsigned)nblk), MOE_PERM_BLOCK, lds, st>>>(topk_idx, T, E, k, blk, diag);
+  perm_scan_kernel<<<1, 1024, 0, st>>>(blk, nblk, E, counts, offsets);
+  perm_scatter_kernel<<<dim3((unsigned)nblk), MOE_PERM_BLOCK, lds, st>>>(topk_idx, T, E, k, blk, row_token,
+                                                                          token_row);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- GEMM tile prefixes
+// tile_off[b][g] = sum_{g' < g} ceil(rows_g' / BM_b) for the routed groups
+// g <= E, and tile_off[b][E+1] adds the shared group's ceil(T / BM_b) m-tiles.
+__global__ __launch_bounds__(1024) void tile_offsets_kernel(const int32_t *__restrict__ counts, int E, int64_t T,
+                                                            int has_shared, int32_t *__restrict__ tile_off) {
+  __shared__ int sh[1024];
+  const int e = threadIdx.x;
+  const int c = e < E ? counts[e] : 0;
+  for (int b = 0; b < MOE_N_BM; ++b) {
+    const int bm = moe_bm_of(b);
+    int all;
+    const int off = block_exclusive_scan(e < E ? (c + bm - 1) / bm : 0, sh, &all);
+    int32_t *to = tile_off + b * (E + 2);
+    if (e < E) to[e] = off;
+    if (e == 0) {
+      to[E] = all;
+      to[E + 1] = all + (has_shared ? (int)((T + bm - 1) / bm) : 0);
+    }
+  }
+}
+
+hipError_t launch_tile_offsets(const moe_dims &dm, int64_t T, const int32_t *counts, const WsLayout &L, char *ws,
+                               hipStream_t st) {
+  tile_offsets_kernel<<<1, 1024, 0, st>>>(counts, dm.n_routed, T, dm.d_ff_shared > 0 ? 1 : 0,
+                                          (int32_t *)(ws + L.tile_off));
+  return hipGetLastError();
+}

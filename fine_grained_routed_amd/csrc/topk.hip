@@ -1,0 +1,307 @@
+// Softmax over all routed experts + per-token top-k with exact ranking.
+//
+// Source: "What is an 'expert', really?" (glossary: the router keeps the top-k;
+// softmax turns raw scores into blend weights that add to 1).  The selection
+// key is the exact real logit of the stored inputs; ties go to the lower
+// expert index; slot j holds the (j+1)-th largest key.  The kept weights are
+// the full-softmax probabilities (not renormalised over the k kept experts).
+//
+// One wavefront per token.  Each of the k rounds picks the largest remaining
+// key.  With computed logits L_e and bounds B_e (router.hip), let m be the
+// largest lower bound L_e - B_e among the remaining experts; only experts with
+// L_e + B_e >= m can hold the maximum.  When that set has one member it is the
+// winner.  Otherwise its members' logits are recomputed in fp64 (exact
+// products, fp64 sums; bound ~(d/64 + 8) 2^-52 ||u|| ||c||) and written back in
+// place with their tighter bounds, and the round is re-decided.  Members whose
+// fp64 intervals still overlap are compared exactly: each key becomes a 256-bit
+// fixed-point sum of its exact products (bf16 x bf16 and fp32 x fp32 products
+// are exact in fp64) and the largest wins, ties to the lower index.  A product
+// that falls below the fixed-point window (a dynamic range above ~2^200 inside
+// one token) raises a diagnostics flag instead of being dropped silently.
+#include "common.h"
+
+double router_bound_coeff(const moe_dims &dm);
+
+#define TOPK_TOKENS_PER_WG 4
+#define EXACT_LIMBS 8  // radix 2^32 digits held in int64 (carry headroom)
+
+template <bool BF16>
+__device__ __forceinline__ double load_elem(const void *p, int64_t i) {
+  if (BF16) return (double)bf16_to_f32(((const uint16_t *)p)[i]);
+  return (double)((const float *)p)[i];
+}
+
+// floor(log2|x|) of a finite non-zero double; a very small sentinel for zero
+__device__ __forceinline__ int exponent_of(double x) {
+  if (x == 0.0) return -100000;
+  const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+  const int ex = (int)((b >> 52) & 0x7ff);
+  if (ex == 0) return -1075;  // subnormal: below every value used here
+  return ex - 1023;
+}
+
+// acc += p exactly as a multiple of 2^E0 (p = mant * 2^lsb).  Sets *bad when a
+// non-zero bit of p falls below 2^E0 or above the window.
+__device__ __forceinline__ void exact_add(long long (&acc)[EXACT_LIMBS], double p, int E0, unsigned &bad) {
+  if (p == 0.0) return;
+  const unsigned long long bits = (unsigned long long)__double_as_longlong(p);
+  const bool neg = (bits >> 63) != 0;
+  int ex = (int)((bits >> 52) & 0x7ff);
+  unsigned long long mant = bits & 0xfffffffffffffull;
+  if (ex == 0) ex = 1; else mant |= 1ull << 52;
+  int sh = (ex - 1075) - E0;
+  if (sh < 0) {
+    if (sh <= -64) { bad = 1u; return; }
+    if (mant & ((1ull << (-sh)) - 1ull)) bad = 1u;
+    mant >>= -sh;
+    sh = 0;
+  }
+  const int li = sh >> 5, off = sh & 31;
+  if (li > EXACT_LIMBS - 3) { bad = 1u; return; }
+  const long long d0 = (long long)((mant << off) & 0xffffffffull);
+  const unsigned long long rem = off ? (mant >> (32 - off)) : (mant >> 32);
+  const long long d1 = (long long)(rem & 0xffffffffull);
+  const long long d2 = (long long)(rem >> 32);
+#pragma unroll
+  for (int q = 0; q < EXACT_LIMBS; ++q) {
+    long long v = (q == li ? d0 : 0) + (q == li + 1 ? d1 : 0) + (q == li + 2 ? d2 : 0);
+    acc[q] += neg ? -v : v;
+  }
+}
+
+// sign of (a - b) for two fixed-point sums on the same window
+__device__ __forceinline__ int exact_cmp(const long long (&a)[EXACT_LIMBS], const long long (&b)[EXACT_LIMBS]) {
+  long long dlt[EXACT_LIMBS];
+#pragma unroll
+  for (int q = 0; q < EXACT_LIMBS; ++q) dlt[q] = a[q] - b[q];
+#pragma unroll
+  for (int q = 0; q < EXACT_LIMBS - 1; ++q) {
+    const long long c = dlt[q] >> 32;  // floor division
+    dlt[q] -= c * (1ll << 32);
+    dlt[q + 1] += c;
+  }
+  if (dlt[EXACT_LIMBS - 1] != 0) return dlt[EXACT_LIMBS - 1] > 0 ? 1 : -1;
+  long long any = 0;
+#pragma unroll
+  for (int q = 0; q < EXACT_LIMBS - 1; ++q) any |= dlt[q];
+  return any != 0 ? 1 : 0;
+}
+
+// Wave-cooperative exact key of expert e for the token row urow (uniform result).
+template <bool BF16>
+__device__ void exact_key(const void *urow, const void *w, const float *bias, int e, int d, int E0,
+                          long long (&key)[EXACT_LIMBS], unsigned &bad) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < EXACT_LIMBS; ++q) key[q] = 0;
+  for (int i = lane; i < d; i += 64) {
+    const double p = load_elem<BF16>(urow, i) * load_elem<BF16>(w, (int64_t)e * d + i);
+    exact_add(key, p, E0, bad);
+  }
+  if (bias && lane == 0) exact_add(key, (double)bias[e], E0, bad);
+#pragma unroll
+  for (int q = 0; q < EXACT_LIMBS; ++q) key[q] = wave_sum_i64(key[q]);
+}
+
+// Wave-cooperative fp64 logit of expert e (uniform result): exact products, fp64 sums.
+template <bool BF16>
+__device__ double dot_f64(const void *urow, const void *w, const float *bias, int e, int d) {
+  const int lane = threadIdx.x & 63;
+  double acc = 0.0;
+  for (int i = lane; i < d; i += 64) acc = fma(load_elem<BF16>(urow, i), load_elem<BF16>(w, (int64_t)e * d + i), acc);
+  acc = wave_sum_f64(acc);
+  if (bias) acc += (double)bias[e];
+  return acc;
+}
+
+template <int S, bool BF16>
+__global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ logits, const double *__restrict__ un2,
+                                                   const double *__restrict__ wn2, const float *__restrict__ bias,
+                                                   const void *__restrict__ u, const void *__restrict__ w,
+                                                   int64_t T, int E, int d, int k, double c1,
+                                                   int32_t *__restrict__ idx_out, float *__restrict__ w_out,
+                                                   DiagWords *diag) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * TOPK_TOKENS_PER_WG + (threadIdx.x >> 6);
+  if (t >= T) return;
+  double L[S], B[S];
+  unsigned avail = 0;
+  const double unorm = un2[t];
+  const double NEG = -__builtin_huge_val();
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int e = lane + 64 * s;
+    if (e < E) {
+      L[s] = logits[t * E + e];
+      B[s] = c1 * sqrt(unorm * wn2[e]) * (1.0 + 0x1p-30) + 0x1p-50 * fabs(L[s]) + d * 0x1p-120;
+      avail |= 1u << s;
+    } else {
+      L[s] = NEG;
+      B[s] = 0.0;
+    }
+  }
+  // softmax statistics over all experts (fp64)
+  double mx = NEG;
+#pragma unroll
+  for (int s = 0; s < S; ++s) mx = fmax(mx, L[s]);
+  mx = wave_max_f64(mx);
+  double sum = 0.0;
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    if (avail & (1u << s)) sum += exp(L[s] - mx);
+  sum = wave_sum_f64(sum);
+
+  const void *urow = BF16 ? (const void *)((const uint16_t *)u + t * d) : (const void *)((const float *)u + t * d);
+  bool token_exact = false;
+  unsigned bad = 0;
+  int eu = -100000;  // max exponent of |u_t,i|, computed on first need
+  const double c64 = (d / 64 + 8) * 0x1p-52;  // fp64 refinement bound coefficient
+  unsigned refined = 0;                         // slots whose L/B hold fp64 values
+  for (int j = 0; j < k; ++j) {
+    int win = -1;
+    for (;;) {
+      double mlo = NEG;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        if (avail & (1u << s)) mlo = fmax(mlo, L[s] - B[s]);
+      mlo = wave_max_f64(mlo);
+      unsigned member = 0;
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        if ((avail & (1u << s)) && L[s] + B[s] >= mlo) member |= 1u << s;
+      const int cnt = wave_sum_i32(__popc(member));
+      if (cnt == 1) {
+        int my = -1;
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+          if (member & (1u << s)) my = lane + 64 * s;
+        win = wave_max_i32(my);
+        break;
+      }
+      token_exact = true;
+      const unsigned need = member & ~refined;
+      if (wave_sum_i32(__popc(need)) > 0) {
+        // level 2: fp64 logits of the unrefined members, written back in place.
+        // Members are visited by a uniform walk over all experts (expert e
+        // lives in lane e % 64, register slot e / 64).
+        for (int e = 0; e < E; ++e) {
+          const unsigned nb = (unsigned)__shfl((int)need, e & 63, 64);
+          if (!((nb >> (e >> 6)) & 1u)) continue;
+          const double l64 = dot_f64<BF16>(urow, w, bias, e, d);
+          const double b64 = c64 * sqrt(unorm * wn2[e]) * (1.0 + 0x1p-30) + 0x1p-51 * fabs(l64) + d * 0x1p-120;
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+            if (lane + 64 * s == e) {
+              L[s] = l64;
+              B[s] = b64;
+              refined |= 1u << s;
+            }
+        }
+        if (lane == 0) atomicAdd(&diag->refinements, 1u);
+        continue;  // re-decide the round with the tighter intervals
+      }
+      // level 3: exact tournament over the (all refined) members, ascending index
+      if (eu == -100000) {
+        int m = -100000;
+        for (int i = lane; i < d; i += 64) m = max(m, exponent_of(load_elem<BF16>(urow, i)));
+        eu = wave_max_i32(m);
+      }
+      int ew = -100000, eb = -100000;
+      for (int e = 0; e < E; ++e) {
+        const unsigned mb = (unsigned)__shfl((int)member, e & 63, 64);
+        if (!((mb >> (e >> 6)) & 1u)) continue;
+        for (int i = lane; i < d; i += 64) ew = max(ew, exponent_of(load_elem<BF16>(w, (int64_t)e * d + i)));
+        if (bias) eb = max(eb, exponent_of((double)bias[e]));
+      }
+      ew = wave_max_i32(ew);
+      eb = __builtin_amdgcn_readfirstlane(eb);
+      int lg = 1;
+      while ((1 << lg) < d + 2) ++lg;
+      const int top = max(eu + ew + 2, eb + 1) + lg + 1;
+      const int E0 = __builtin_amdgcn_readfirstlane(top - 240);
+      long long best[EXACT_LIMBS];
+      long long cur[EXACT_LIMBS];
+      int wn = -1;
+#pragma unroll
+      for (int q = 0; q < EXACT_LIMBS; ++q) best[q] = 0;
+      for (int e = 0; e < E; ++e) {
+        const unsigned mb = (unsigned)__shfl((int)member, e & 63, 64);
+        if (!((mb >> (e >> 6)) & 1u)) continue;
+        exact_key<BF16>(urow, w, bias, e, d, E0, cur, bad);
+        // keys are wave sums: make their uniformity explicit before comparing
+        int better = 0;
+        if (wn >= 0) better = exact_cmp(cur, best) > 0 ? 1 : 0;
+        better = __builtin_amdgcn_readfirstlane(better);
+        if (wn < 0 || better) {
+          wn = e;
+#pragma unroll
+          for (int q = 0; q < EXACT_LIMBS; ++q) best[q] = cur[q];
+        }
+      }
+      win = __builtin_amdgcn_readfirstlane(wn);
+      if (lane == 0) atomicAdd(&diag->exact_keys, (unsigned)cnt);
+      break;
+    }
+    // take the winner out and emit its slot
+    double lw = NEG;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if (lane + 64 * s == win) {
+        lw = L[s];
+        avail &= ~(1u << s);
+      }
+    lw = wave_max_f64(lw);
+    if (lane == 0) {
+      idx_out[t * k + j] = win;
+      w_out[t * k + j] = (float)(exp(lw - mx) / sum);
+    }
+  }
+  if (lane == 0) {
+    if (token_exact) atomicAdd(&diag->tokens_exact, 1u);
+  }
+  bad = (unsigned)wave_max_i32((int)bad);
+  if (lane == 0 && bad) atomicOr(&diag->flags, MOE_DIAG_UNRESOLVED);
+}
+
+template <int S>
+static void launch_topk_s(const moe_dims &dm, int64_t T, const void *u, const void *w, const float *bias,
+                          int32_t *idx, float *wout, const WsLayout &L, char *ws, hipStream_t st) {
+  const double c1 = router_bound_coeff(dm);
+  dim3 grid((unsigned)((T + TOPK_TOKENS_PER_WG - 1) / TOPK_TOKENS_PER_WG));
+  const double *lg = (const double *)(ws + L.logits);
+  const double *un2 = (const double *)(ws + L.unorm2);
+  const double *wn2 = (const double *)(ws + L.wnorm2);
+  DiagWords *diag = (DiagWords *)(ws + L.diag);
+  if (dm.dtype == MOE_BF16)
+    topk_kernel<S, true><<<grid, 256, 0, st>>>(lg, un2, wn2, bias, u, w, T, dm.n_routed, dm.d_model, dm.top_k, c1,
+                                               idx, wout, diag);
+  else
+    topk_kernel<S, false><<<grid, 256, 0, st>>>(lg, un2, wn2, bias, u, w, T, dm.n_routed, dm.d_model, dm.top_k, c1,
+                                                idx, wout, diag);
+}
+
+hipError_t launch_topk(const moe_dims &dm, int64_t T, const void *u, const void *w_router, const float *bias,
+                       int32_t *topk_idx, float *topk_w, const WsLayout &L, char *ws, hipStream_t st) {
+  const int E = dm.n_routed;
+  if (E <= 64) launch_topk_s<1>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
+  else if (E <= 128) launch_topk_s<2>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
+  else if (E <= 256) launch_topk_s<4>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
+  else if (E <= 512) launch_topk_s<8>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
+  else launch_topk_s<16>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------- diagnostics
+__global__ void diag_clear_kernel(DiagWords *d) {
+  if (threadIdx.x == 0) {
+    d->flags = 0;
+    d->tokens_exact = 0;
+    d->exact_keys = 0;
+    d->refinements = 0;
+  }
+}
+
+hipError_t launch_diag_clear(void *ws, hipStream_t st) {
+  diag_clear_kernel<<<1, 64, 0, st>>>((DiagWords *)ws);
+  return hipGetLastError();
+}

@@ -1,0 +1,174 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) library for the forward pass of one
+ * DeepSeekMoE-style mixture-of-experts FFN layer: a softmax top-k router over
+ * N_r fine-grained routed SwiGLU experts plus N_s always-on shared SwiGLU
+ * experts fused into one MLP of width N_s*f.
+ *
+ * What the layer computes (sources: "Shared Expert" page on DeepSeek-V3, How
+ * it works, eq. 12 without its residual term, and the SwiGLU definition;
+ * Official code: MoE.forward returns shared + routed on the flattened (T, d)
+ * batch; "What is an 'expert', really?", glossary and panel 2: a linear
+ * router scores the experts, softmax makes blend weights, the top-k are kept):
+ *
+ *   l[t,e]  = u[t,:] . w_router[e,:] (+ router_bias[e])
+ *   p[t,:]  = softmax over all N_r experts of l[t,:]
+ *   S_t     = the k largest l[t,e] (ties to the lower e), slots in descending order
+ *   out[t]  = FFN_shared(u[t]) + sum_{j<k} p[t,S_t[j]] * FFN_{S_t[j]}(u[t])
+ *   FFN(x)  = W2 (SiLU(W1 x) * W3 x),   SiLU(z) = z * sigmoid(z)
+ *
+ * The kept gates are NOT renormalised; the shared MLP enters with coefficient
+ * exactly 1; no residual is added and no normalisation is applied (u arrives
+ * already RMS-normalised).  Every token goes to all k of its experts (no
+ * capacity limit).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host).  Every array is dense,
+ *     row-major, 16-byte aligned.  Weights use the [out, in] layout:
+ *       w_router [N_r, d]; w1, w3 [N_r, f, d]; w2 [N_r, d, f];
+ *       w1s, w3s [f_s, d]; w2s [d, f_s]; router_bias [N_r] fp32.
+ *   - The caller owns every buffer, including the workspace `ws` (size from
+ *     moe_workspace_size).  The library allocates and frees nothing and keeps
+ *     no state between calls; calls on different streams with different
+ *     workspaces may run concurrently.
+ *   - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL =
+ *     the default stream).  No call copies device data to the host, except
+ *     moe_read_diagnostics, which synchronises the stream.
+ *   - Arguments are validated on the host before any HIP call.  A failing
+ *     call returns a non-zero moe_status, enqueues nothing, and leaves a
+ *     message in moe_last_error().  T == 0 is a valid no-op.
+ *   - Faults inside a kernel surface at the caller's next synchronisation.
+ *
+ * Limits: 1 <= top_k <= 16; 1 <= n_routed <= 1024; top_k <= n_routed;
+ * d_model and d_ff (and d_ff_shared when non-zero) multiples of 64;
+ * 64 <= d_model <= 32768; T * top_k < 2^31.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_VALUE = 1, /* null pointer, negative T, top_k > n_routed, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = 2,   /* a size or dtype outside the limits above */
+  MOE_ERR_WORKSPACE = 3,     /* ws_bytes smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4            /* a HIP launch or runtime call failed; text in moe_last_error() */
+} moe_status;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer shape.  dtype applies to u and to every weight (the router bias is
+ * always fp32).  bf16 inputs are multiplied on bf16 matrix cores with fp32
+ * accumulation; fp32 inputs use fp32 arithmetic throughout. */
+typedef struct moe_dims {
+  int32_t d_model;     /* d */
+  int32_t n_routed;    /* N_r */
+  int32_t d_ff;        /* f, width of one routed expert */
+  int32_t d_ff_shared; /* f_s = N_s * f, width of the fused shared MLP; 0 = no shared expert */
+  int32_t top_k;       /* k */
+  int32_t dtype;       /* moe_dtype of u and the weights */
+  int32_t out_dtype;   /* moe_dtype of `out` (MOE_F32 recommended) */
+} moe_dims;
+
+/* Device pointers to the layer's weights (layouts above).  router_bias may be
+ * NULL (no bias); w1s, w3s, w2s must be NULL exactly when d_ff_shared == 0. */
+typedef struct moe_weights {
+  const void *w_router;
+  const float *router_bias;
+  const void *w1, *w3, *w2;
+  const void *w1s, *w3s, *w2s;
+} moe_weights;
+
+/* Path choice and optional stage timing.
+ *   path: 0 = automatic (decode path when T*top_k <= 2*n_routed and T <= 256,
+ *         else prefill), 1 = prefill (tiled grouped GEMMs), 2 = decode
+ *         (weight-streaming kernels over the experts that received tokens).
+ *   events (host array of n_events hipEvent_t, may be NULL): when non-NULL the
+ *   library records events[i] on `stream` at stage boundaries, in this order:
+ *   0 start, 1 after router logits, 2 after top-k, 3 after permutation,
+ *   4 after gate/up, 5 after down, 6 after combine (moe_layer_forward), or
+ *   0 start, 1 after gate/up, 2 after down (moe_expert_ffn).  Boundaries
+ *   beyond n_events are not recorded. */
+typedef struct moe_options {
+  int32_t path;
+  int32_t n_events;
+  void **events;
+} moe_options;
+
+/* Diagnostics written by the kernels into the workspace header. */
+typedef struct moe_diag {
+  uint32_t flags;           /* bit 0: a top-k comparison could not be settled exactly
+                               bit 1: topk_idx held an index outside [0, N_r) (skipped)
+                               bit 2: topk_idx held a duplicate expert in one row */
+  uint32_t tokens_exact;    /* tokens with a top-k comparison the first-level bound left open */
+  uint32_t exact_keys;      /* exact fixed-point logits evaluated (comparisons fp64 left open) */
+  uint32_t refinements;     /* fp64 logit recomputation passes */
+} moe_diag;
+
+/* Workspace needed by every call below for this shape and token count (host out). */
+moe_status moe_workspace_size(const moe_dims *dims, int64_t T, size_t *bytes);
+
+/* Router: logits, softmax over all N_r experts, per-token top-k.
+ * Writes topk_idx [T, k] int32 (slot 0 = largest logit; ties to the lower
+ * expert index; the selection and slot order equal those of the exact real
+ * logits of the stored inputs) and topk_w [T, k] fp32 = the full-softmax
+ * probability of each kept expert.
+ * Source: "What is an 'expert', really?" (glossary: router, top-k, softmax;
+ * panel 2) and "Shared Expert" (How it works: the N_r centroids). */
+moe_status moe_router_topk(const moe_dims *dims, int64_t T, const void *u, const void *w_router,
+                           const float *router_bias, int32_t *topk_idx, float *topk_w,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* Permutation: group the T*k (token, slot) pairs by expert.
+ * counts [N_r] = pairs per expert; offsets [N_r+1] exclusive prefix of counts
+ * (offsets[N_r] = T*k); row_token [T*k]: rows offsets[e]..offsets[e+1]-1 hold
+ * the tokens that chose e in ascending token order; token_row [T, k]: the row
+ * of token t's slot j.  Deterministic and bit-exact.  Each row of topk_idx must
+ * hold k distinct experts in [0, N_r); violations set moe_diag.flags.
+ * Source: "Shared Expert" (How it works: scatter-sum of routed outputs). */
+moe_status moe_permute(const moe_dims *dims, int64_t T, const int32_t *topk_idx, int32_t *counts,
+                       int32_t *offsets, int32_t *row_token, int32_t *token_row,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Expert FFNs: y_rows[r,:] = FFN_e(u[row_token[r],:]) for every row r of every
+ * expert group e (fp32 [T*k, d]), and y_shared[t,:] = shared MLP of u[t,:]
+ * (fp32 [T, d]) when the layer has shared experts (else y_shared must be NULL).
+ * counts/offsets/row_token are moe_permute's outputs.
+ * Source: "Shared Expert" (How it works: SwiGLU; Official code: fused shared
+ * MLP of width N_s*f on the full batch); "Shared and fine-grained experts"
+ * (Researcher level, Systems limits: grouped GEMM over many small experts). */
+moe_status moe_expert_ffn(const moe_dims *dims, int64_t T, const void *u, const moe_weights *w,
+                          const int32_t *counts, const int32_t *offsets, const int32_t *row_token,
+                          float *y_rows, float *y_shared, const moe_options *opts,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* Combine: out[t,:] = y_shared[t,:] + sum_{j=0..k-1} topk_w[t,j] * y_rows[token_row[t,j],:],
+ * accumulated in fp32 in exactly this order (y_shared NULL: start from 0),
+ * written as out_dtype.  Source: "Shared Expert" (How it works: shared output
+ * added to the scatter-sum of routed outputs; Watch-outs: coefficient 1). */
+moe_status moe_combine(const moe_dims *dims, int64_t T, const float *y_rows, const float *y_shared,
+                       const float *topk_w, const int32_t *token_row, void *out, void *stream);
+
+/* The whole layer: router, permutation, expert FFNs, combine; `out` [T, d] in
+ * out_dtype receives shared + routed (no residual).  Intermediates live in ws. */
+moe_status moe_layer_forward(const moe_dims *dims, int64_t T, const void *u, const moe_weights *w,
+                             void *out, const moe_options *opts, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* Copy the diagnostics of the last call that used `ws` to *diag (host);
+ * synchronises `stream`.  Intended for tests. */
+moe_status moe_read_diagnostics(const void *ws, moe_diag *diag, void *stream);
+
+/* Message of the last failing call on this thread (library-owned storage). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

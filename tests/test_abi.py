@@ -1,0 +1,145 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fine_grained_routed_amd as fgr
+from fine_grained_routed_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20  # an aligned, never-dereferenced address: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fgr.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^(?:moe_status|const char \*)\s*(moe_\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    for name in ("moe_router_topk", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward"):
+        assert name in fns
+    assert set(fns) == set(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(lib.path)
+    for name in header_functions():
+        assert hasattr(raw, name), name
+
+
+def test_struct_sizes_match_header():
+    assert ctypes.sizeof(B.Dims) == 28
+    assert ctypes.sizeof(B.Weights) == 64
+    assert ctypes.sizeof(B.Diag) == 16
+
+
+def _dims(lib, **kw):
+    a = dict(d_model=128, n_routed=8, d_ff=64, d_ff_shared=64, top_k=2, dtype=fgr.MOE_BF16, out_dtype=fgr.MOE_F32)
+    a.update(kw)
+    return lib.dims(**a)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=9), B.MOE_ERR_INVALID_VALUE),        # k > N_r
+    (dict(top_k=0), B.MOE_ERR_INVALID_VALUE),
+    (dict(n_routed=0), B.MOE_ERR_INVALID_VALUE),
+    (dict(top_k=17, n_routed=64), B.MOE_ERR_UNSUPPORTED),
+    (dict(n_routed=1025), B.MOE_ERR_UNSUPPORTED),
+    (dict(dtype=7), B.MOE_ERR_UNSUPPORTED),
+    (dict(out_dtype=3), B.MOE_ERR_UNSUPPORTED),
+    (dict(d_model=100), B.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff=96), B.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff_shared=32), B.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff_shared=-64), B.MOE_ERR_INVALID_VALUE),
+])
+def test_bad_dims(lib, kw, status):
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.workspace_size(_dims(lib, **kw), 16)
+    assert ei.value.status == status
+    assert lib.last_error()
+
+
+def test_negative_T_and_huge_T(lib):
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.workspace_size(_dims(lib), -1)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.workspace_size(_dims(lib, top_k=8), 1 << 28)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_size_grows_with_T(lib):
+    d = _dims(lib)
+    assert lib.workspace_size(d, 0) > 0
+    assert lib.workspace_size(d, 1000) > lib.workspace_size(d, 10)
+
+
+def test_T_zero_is_a_noop_even_with_null_pointers(lib):
+    d = _dims(lib)
+    lib.layer_forward(d, 0, None, lib.weights(), None, None, None, ws_bytes=0, stream=0)
+    lib.router_topk(d, 0, None, None, None, None, None, None, ws_bytes=0, stream=0)
+    lib.permute(d, 0, None, None, None, None, None, None, ws_bytes=0, stream=0)
+    lib.combine(d, 0, None, None, None, None, None, stream=0)
+
+
+def _full_weights(lib, shared=True):
+    return lib.weights(FAKE, None, FAKE, FAKE, FAKE, FAKE if shared else None, FAKE if shared else None,
+                       FAKE if shared else None)
+
+
+def test_null_and_misaligned_pointers(lib):
+    d = _dims(lib)
+    ws_bytes = lib.workspace_size(d, 4)
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.layer_forward(d, 4, None, _full_weights(lib), FAKE, None, FAKE, ws_bytes=ws_bytes, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE and "u" in str(ei.value)
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.layer_forward(d, 4, FAKE + 2, _full_weights(lib), FAKE, None, FAKE, ws_bytes=ws_bytes, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE and "aligned" in str(ei.value)
+    with pytest.raises(fgr.MoeError) as ei:  # shared experts declared, shared weights missing
+        lib.layer_forward(d, 4, FAKE, _full_weights(lib, shared=False), FAKE, None, FAKE, ws_bytes=ws_bytes, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE and "w1s" in str(ei.value)
+    d0 = _dims(lib, d_ff_shared=0)
+    with pytest.raises(fgr.MoeError) as ei:  # shared weights given, no shared experts declared
+        lib.layer_forward(d0, 4, FAKE, _full_weights(lib), FAKE, None, FAKE, ws_bytes=ws_bytes, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.router_topk(d, 4, FAKE, FAKE, FAKE + 1, FAKE, FAKE, FAKE, ws_bytes=ws_bytes, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE  # misaligned bias
+
+
+def test_workspace_too_small(lib):
+    d = _dims(lib)
+    need = lib.workspace_size(d, 4)
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.layer_forward(d, 4, FAKE, _full_weights(lib), FAKE, None, FAKE, ws_bytes=need - 1, stream=0)
+    assert ei.value.status == B.MOE_ERR_WORKSPACE
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.permute(d, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes=16, stream=0)
+    assert ei.value.status == B.MOE_ERR_WORKSPACE
+
+
+def test_bad_options(lib):
+    d = _dims(lib)
+    need = lib.workspace_size(d, 4)
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.layer_forward(d, 4, FAKE, _full_weights(lib), FAKE, lib.options(path=5), FAKE, ws_bytes=need, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE
+    bad = B.Options(0, 3, None)
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.layer_forward(d, 4, FAKE, _full_weights(lib), FAKE, bad, FAKE, ws_bytes=need, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(FileNotFoundError):
+        B.Library(str(tmp_path / "libmoe.so"))

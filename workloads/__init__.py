@@ -44,6 +44,7 @@ __all__ = [
     "to_f64",
     "sample_tokens",
     "ROW_BLOCK",
+    "F64Experts",
 ]
 
 ROW_BLOCK = 64  # rows of u drawn per generator
@@ -191,3 +192,18 @@ def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
     n = min(n, T)
     rng = np.random.default_rng([seed, T, n, 7])
     return np.sort(rng.choice(T, size=n, replace=False)).astype(np.int64)
+
+
+class F64Experts:
+    """Indexable view of a stacked weight tensor [E, ...] (any device) whose
+    item e is expert e's matrix as a host fp64 array (exact widening).  Lets
+    the oracle walk large expert stacks one expert at a time."""
+
+    def __init__(self, t: torch.Tensor):
+        self.t = t
+
+    def __len__(self):
+        return self.t.shape[0]
+
+    def __getitem__(self, e: int) -> np.ndarray:
+        return self.t[e].to(torch.float64).to("cpu").numpy()
