@@ -105,6 +105,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (3 times): the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -116,6 +118,15 @@ def main():
     from fine_grained_routed_amd import PATH_AUTO, PATH_DECODE, MoELayer
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_dispatch": n * 4, "dispatches": 3}), flush=True)
+        return
     wl = workloads.get(args.workload)
     print(f"[bench] drawing inputs for {wl.name}", file=sys.stderr, flush=True)
     inp = workloads.make_inputs(wl, seed=args.seed, device="cuda")

@@ -21,32 +21,36 @@
 // 256 fp32 accumulators per lane.  A wave skips the 32-row sub-tiles past the
 // group's last row, so a ragged tail costs in proportion to its rows.  Both
 // operands are K-contiguous; LDS rows of 64 bf16 hold their 16-byte chunks
-// XOR-swizzled by (row % 8) so that the 16-byte fragment reads of 8
-// consecutive rows hit distinct banks.  Two LDS stages (128 KB) filled by
-// direct global-to-LDS loads (global_load_lds_dwordx4: each lane's 16 bytes
-// land at LDS base + 16 * lane, so the swizzle is applied by choosing which
-// global chunk each lane fetches): the next k-tile streams into the idle
-// stage while the current one is multiplied, with no staging registers.
-// Rows past the group and columns past N read clamped in-bounds addresses;
-// their products only reach outputs that are never stored.  One work-group
-// per CU.
+// XOR-swizzled per row so that fragment reads are free of bank conflicts.
+// LDS is filled by direct global-to-LDS loads (global_load_lds_dwordx4: each
+// lane's 16 bytes land at LDS base + 16 * lane, so the swizzle is applied by
+// choosing which global chunk each lane fetches), with no staging registers;
+// every row segment fetched is a whole 128-byte line.  The token-row tile is
+// fetched one k-tile ahead (it is shared by all column tiles of the XCD and
+// mostly hits in L2) and the weight tile two k-tiles ahead.  The barrier that
+// publishes tile j + 1 sits before the last 16-deep step of tile j, so the
+// first fragment reads of tile j + 1 overlap the last MFMAs of tile j.
+// One work-group per CU.
 //
 // The grid covers an upper bound of the tile count; each work-group reads the
 // device-side tile prefixes (256-row tiles), so no host sync is needed.
-// Work-groups are remapped so that each XCD (8 per chip, dispatched
-// round-robin) walks a contiguous range of tiles, column tiles fastest: the
-// 32 CUs of an XCD then work on one expert at a time, sharing its token rows
-// and weight panels in that XCD's L2.
+// Work-groups are dispatched round-robin over the 8 XCDs, so work-group i is
+// remapped to tile (i % 8) * ceil(total / 8) + i / 8: each XCD walks a
+// contiguous range of the tile order described in the kernel, and the 32 CUs
+// of an XCD work on one expert at a time, sharing its token rows and weight
+// panels in that XCD's L2.
 #include <algorithm>
 
 #include "common.h"
 
 #define PF_BM 256
-#define PF_BN 256   // B rows per tile (gate/up: 128 gate + 128 up)
+#define PF_BN 256    // B rows per tile (gate/up: 128 gate + 128 up)
 #define PF_BK 64
 #define PF_BM_IDX 4  // moe_bm_of(4) == 256
 #define PF_MT 8      // 32-row sub-tiles per tile
-#define PF_LOADS 8   // 16-byte chunks per lane per operand per k-tile (8 rows per wave instruction)
+#define PF_GM 8      // m-tiles per ordering block (routed experts)
+#define PF_GM_SH 4   // m-tiles per ordering block (shared group)
+#define PF_LOADS 8   // DMA instructions per wave per operand per k-tile (8 rows of 128 B each)
 
 struct GemmArgs {
   const uint16_t *A;         // gate/up: u [T, d]; down: H [R, f]
@@ -66,101 +70,127 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// element offset of 16-byte chunk c of LDS row r (rows of 64 bf16)
-__device__ __forceinline__ int lds_off(int r, int c) { return r * PF_BK + ((c ^ (r & 7)) << 3); }
+// LDS rows of 64 bf16 hold eight 16-byte chunks; chunk c of row r sits in slot
+// c ^ swz(r).  swz is one-to-one on any 8 consecutive rows and on any 8 rows
+// of one parity among 16 consecutive rows, so the 16-byte fragment reads of 8
+// (or 16) consecutive rows fall on distinct banks whether the LDS serves 8
+// lanes over 32 banks or 16 lanes over 64 banks per cycle.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// element offset of 16-byte chunk c of LDS row r
+__device__ __forceinline__ int lds_off(int r, int c) { return r * PF_BK + ((c ^ swz(r)) << 3); }
 
 // 16 bytes per lane from global memory straight into LDS at dst + 16 * lane
 __device__ __forceinline__ void dma16(const uint16_t *src, uint16_t *dst) {
   __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_t *)dst, 16, 0, 0);
 }
 
-__device__ __forceinline__ void wait_dma_and_sync() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+// Publish LDS to the work-group: this wave's LDS reads are complete and at
+// most one k-tile of B DMA (8 instructions) is still in flight, then the
+// work-group barrier.  Written out rather than __syncthreads(), whose release
+// fence would also wait for every DMA in flight and so drain the prefetch.
+__device__ __forceinline__ void publish() {
+  // s_waitcnt immediate (gfx9 layout: vmcnt [3:0] and [15:14], expcnt [6:4],
+  // lgkmcnt [11:8]): vmcnt 8, expcnt 7, lgkmcnt 0.  The builtin, unlike
+  // inline asm, is visible to the compiler's own wait tracking, which then
+  // knows that older DMA into a stage has landed.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0078);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// LDS stages: four distinct objects, so that the compiler can tell the stage
-// being filled by DMA from the stage being read.
+// LDS: the token-row tile rotates over 2 stages, the weight tile over 3
+// (5 x 32 KB = 160 KB).  Separate objects, so that the compiler can tell a
+// stage being filled by DMA from a stage being read.
 __shared__ __attribute__((aligned(16))) uint16_t g_As0[PF_BM * PF_BK];
 __shared__ __attribute__((aligned(16))) uint16_t g_As1[PF_BM * PF_BK];
 __shared__ __attribute__((aligned(16))) uint16_t g_Bs0[PF_BN * PF_BK];
 __shared__ __attribute__((aligned(16))) uint16_t g_Bs1[PF_BN * PF_BK];
+__shared__ __attribute__((aligned(16))) uint16_t g_Bs2[PF_BN * PF_BK];
 
-template <int ST>
-__device__ __forceinline__ uint16_t *stage_a() { return ST == 0 ? g_As0 : g_As1; }
-template <int ST>
-__device__ __forceinline__ uint16_t *stage_b() { return ST == 0 ? g_Bs0 : g_Bs1; }
+template <int SA>
+__device__ __forceinline__ uint16_t *stage_a() { return SA == 0 ? g_As0 : g_As1; }
+template <int SB>
+__device__ __forceinline__ uint16_t *stage_b() { return SB == 0 ? g_Bs0 : SB == 1 ? g_Bs1 : g_Bs2; }
 
-// Issue the DMA of the k-tile starting at k0 into stage ST.  Wave w fills LDS
-// rows 64w + 8q .. 64w + 8q + 7 (q < 8) of each operand; lane l writes row
-// 64w + 8q + l/8, slot l%8, which holds global chunk (l%8) ^ (l/8).
-template <int MTV, int ST>
-__device__ __forceinline__ void issue_tile(const uint16_t *const (&ap)[PF_LOADS],
-                                           const uint16_t *const (&bp)[PF_LOADS], int k0) {
+// DMA of one operand's k-tile at k0.  Wave w fills LDS rows 64w + 8q ..
+// 64w + 8q + 7 (q < 8); lane l writes row 64w + 8q + l/8, slot l%8, which
+// holds global chunk (l%8) ^ swz(row) (the per-q chunk is folded into src[q]).
+__device__ __forceinline__ void issue_op(const uint16_t *const (&src)[PF_LOADS], uint16_t *stage, int k0) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
-  for (int q = 0; q < PF_LOADS; ++q) {
-    if (64 * wv + 8 * q < 32 * MTV) dma16(ap[q] + k0, stage_a<ST>() + (64 * wv + 8 * q) * PF_BK);
-    dma16(bp[q] + k0, stage_b<ST>() + (64 * wv + 8 * q) * PF_BK);
+  for (int q = 0; q < PF_LOADS; ++q) dma16(src[q] + k0, stage + (64 * wv + 8 * q) * PF_BK);
+}
+
+// Fragments of one 16-deep step: two B column tiles and MTV A row tiles.
+template <int MTV>
+struct Frags {
+  bf16x8_t b0, b1, a[MTV];
+};
+
+template <int MTV, int SA, int SB>
+__device__ __forceinline__ void read_frags(Frags<MTV> &f, int brow0, int brow1, int step) {
+  const uint16_t *As = stage_a<SA>();
+  const uint16_t *Bs = stage_b<SB>();
+  const int lane = threadIdx.x & 63;
+  const int frow = lane & 31;             // fragment row inside a 32-row tile
+  const int ch = step * 2 + (lane >> 5);  // chunk: first/second 8 of the 16-deep step
+  f.b0 = as_bf16x8(*(const uint4 *)&Bs[lds_off(brow0 + frow, ch)]);
+  f.b1 = as_bf16x8(*(const uint4 *)&Bs[lds_off(brow1 + frow, ch)]);
+#pragma unroll
+  for (int i = 0; i < MTV; ++i) f.a[i] = as_bf16x8(*(const uint4 *)&As[lds_off(i * 32 + frow, ch)]);
+}
+
+template <int MTV>
+__device__ __forceinline__ void mfma_step(const Frags<MTV> &f, f32x16_t (&acc)[PF_MT][2]) {
+#pragma unroll
+  for (int i = 0; i < MTV; ++i) {
+    acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b0, acc[i][0], 0, 0, 0);
+    acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b1, acc[i][1], 0, 0, 0);
   }
 }
 
-struct Frags {
-  bf16x8_t b0, b1;
-};
+// MFMAs of one step in pairs, each pair followed by one fragment read of the next step
+template <int MTV>
+__device__ __forceinline__ void interleave_hint() {
+#pragma unroll
+  for (int i = 0; i < MTV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+}
 
-// One k-tile: multiply stage ST while the next tile streams into the other
-// stage.  Fragments of 16-deep step ks+1 are read while step ks multiplies.
-template <int MTV, int ST>
-__device__ __forceinline__ void k_step(const uint16_t *const (&ap)[PF_LOADS], const uint16_t *const (&bp)[PF_LOADS],
-                                       int brow0, int brow1, int k_next, bool has_next,
+// One k-tile j, its token rows in A-stage SA (= j % 2) and weights in B-stage
+// SB (= j % 3).  f0 holds its step-0 fragments on entry and the next tile's
+// step-0 fragments on exit.  Every iteration issues exactly one A tile (j + 1)
+// and one B tile (j + 2) of DMA, past the end re-fetching the last tile into
+// a stage nobody reads again, so the count of DMA in flight is the same on
+// every path and one constant wait publishes tile j + 1.
+template <int MTV, int SA, int SB>
+__device__ __forceinline__ void k_iter(const uint16_t *const (&ap)[PF_LOADS], const uint16_t *const (&bp)[PF_LOADS],
+                                       int brow0, int brow1, int j, int nk, Frags<MTV> &f0, Frags<MTV> &f1,
                                        f32x16_t (&acc)[PF_MT][2]) {
-  if (has_next) issue_tile<MTV, 1 - ST>(ap, bp, k_next);
-  const uint16_t *As = stage_a<ST>();
-  const uint16_t *Bs = stage_b<ST>();
-  const int lane = threadIdx.x & 63;
-  const int frow = lane & 31;    // fragment row inside a 32-row tile
-  const int fchunk = lane >> 5;  // 0/1: first/second 8 of a 16-deep step
-  bf16x8_t b0 = as_bf16x8(*(const uint4 *)&Bs[lds_off(brow0 + frow, fchunk)]);
-  bf16x8_t b1 = as_bf16x8(*(const uint4 *)&Bs[lds_off(brow1 + frow, fchunk)]);
-  bf16x8_t av[MTV];
-#pragma unroll
-  for (int i = 0; i < MTV; ++i) av[i] = as_bf16x8(*(const uint4 *)&As[lds_off(i * 32 + frow, fchunk)]);
-#pragma unroll
-  for (int ks = 0; ks < PF_BK / 16; ++ks) {
-    bf16x8_t nb0, nb1, nav[MTV];
-    if (ks + 1 < PF_BK / 16) {
-      const int ch = (ks + 1) * 2 + fchunk;
-      nb0 = as_bf16x8(*(const uint4 *)&Bs[lds_off(brow0 + frow, ch)]);
-      nb1 = as_bf16x8(*(const uint4 *)&Bs[lds_off(brow1 + frow, ch)]);
-#pragma unroll
-      for (int i = 0; i < MTV; ++i) nav[i] = as_bf16x8(*(const uint4 *)&As[lds_off(i * 32 + frow, ch)]);
-    }
-#pragma unroll
-    for (int i = 0; i < MTV; ++i) {
-      acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], b0, acc[i][0], 0, 0, 0);
-      acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], b1, acc[i][1], 0, 0, 0);
-    }
-    if (ks + 1 < PF_BK / 16) {
-      b0 = nb0;
-      b1 = nb1;
-#pragma unroll
-      for (int i = 0; i < MTV; ++i) av[i] = nav[i];
-    }
-  }
-  // Schedule: the first step's fragment reads, then for every step its MFMAs
-  // in pairs, each pair followed by one fragment read of the next step.
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 + MTV, 0);
-#pragma unroll
-  for (int ks = 0; ks < PF_BK / 16; ++ks) {
-#pragma unroll
-    for (int i = 0; i < MTV; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      if (ks + 1 < PF_BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if (ks + 1 < PF_BK / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  }
-  wait_dma_and_sync();
+  // stages of tile j - 1 (read completely before the previous barrier)
+  issue_op(ap, stage_a<SA ^ 1>(), min(j + 1, nk - 1) * PF_BK);
+  issue_op(bp, stage_b<(SB + 2) % 3>(), min(j + 2, nk - 1) * PF_BK);
+  read_frags<MTV, SA, SB>(f1, brow0, brow1, 1);
+  mfma_step<MTV>(f0, acc);
+  interleave_hint<MTV>();
+  read_frags<MTV, SA, SB>(f0, brow0, brow1, 2);
+  mfma_step<MTV>(f1, acc);
+  interleave_hint<MTV>();
+  read_frags<MTV, SA, SB>(f1, brow0, brow1, 3);
+  mfma_step<MTV>(f0, acc);
+  interleave_hint<MTV>();
+  // publish tile j + 1 (A issued last iteration... this one; B two iterations ago)
+  publish();
+  // step-0 fragments of tile j + 1 (after the last tile this reads stages
+  // whose values are never used; reading LDS is always in bounds)
+  read_frags<MTV, SA ^ 1, (SB + 1) % 3>(f0, brow0, brow1, 0);
+  mfma_step<MTV>(f1, acc);
+  interleave_hint<MTV>();
 }
 
 // The k loop of one tile with MTV valid 32-row sub-tiles (compile-time, so
@@ -169,19 +199,42 @@ template <int MTV>
 __device__ __forceinline__ void k_loop(const uint16_t *const (&ap)[PF_LOADS], const uint16_t *const (&bp)[PF_LOADS],
                                        int brow0, int brow1, int K, f32x16_t (&acc)[PF_MT][2]) {
   const int nk = K / PF_BK;
-  issue_tile<MTV, 0>(ap, bp, 0);
-  wait_dma_and_sync();
-  for (int kt = 0; kt < nk; kt += 2) {
-    k_step<MTV, 0>(ap, bp, brow0, brow1, (kt + 1) * PF_BK, kt + 1 < nk, acc);
-    if (kt + 1 < nk) k_step<MTV, 1>(ap, bp, brow0, brow1, (kt + 2) * PF_BK, kt + 2 < nk, acc);
+  issue_op(ap, stage_a<0>(), 0);
+  issue_op(bp, stage_b<0>(), 0);
+  issue_op(bp, stage_b<1>(), min(1, nk - 1) * PF_BK);
+  publish();  // tile 0 landed; B tile 1 may be in flight
+  Frags<MTV> f0, f1;
+  read_frags<MTV, 0, 0>(f0, brow0, brow1, 0);
+  // six k-tiles per trip (the stage pattern repeats every lcm(2, 3) tiles);
+  // whole trips are unconditional, the remainder follows
+  int j = 0;
+  for (; j + 6 <= nk; j += 6) {
+    k_iter<MTV, 0, 0>(ap, bp, brow0, brow1, j, nk, f0, f1, acc);
+    k_iter<MTV, 1, 1>(ap, bp, brow0, brow1, j + 1, nk, f0, f1, acc);
+    k_iter<MTV, 0, 2>(ap, bp, brow0, brow1, j + 2, nk, f0, f1, acc);
+    k_iter<MTV, 1, 0>(ap, bp, brow0, brow1, j + 3, nk, f0, f1, acc);
+    k_iter<MTV, 0, 1>(ap, bp, brow0, brow1, j + 4, nk, f0, f1, acc);
+    k_iter<MTV, 1, 2>(ap, bp, brow0, brow1, j + 5, nk, f0, f1, acc);
   }
+  if (j < nk) k_iter<MTV, 0, 0>(ap, bp, brow0, brow1, j, nk, f0, f1, acc);
+  if (j + 1 < nk) k_iter<MTV, 1, 1>(ap, bp, brow0, brow1, j + 1, nk, f0, f1, acc);
+  if (j + 2 < nk) k_iter<MTV, 0, 2>(ap, bp, brow0, brow1, j + 2, nk, f0, f1, acc);
+  if (j + 3 < nk) k_iter<MTV, 1, 0>(ap, bp, brow0, brow1, j + 3, nk, f0, f1, acc);
+  if (j + 4 < nk) k_iter<MTV, 0, 1>(ap, bp, brow0, brow1, j + 4, nk, f0, f1, acc);
+  // the trailing re-fetches must land before the work-group can exit
+  __builtin_amdgcn_s_waitcnt(0x0070);
 }
 
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
-  // ---- tile lookup (XCD-contiguous order, column tiles fastest)
+  // ---- tile lookup.  Order: group by group; inside a group, blocks of up to
+  // PF_GM m-tiles (PF_GM_SH for the shared group), and inside a block the
+  // m-tiles fastest, so the tiles that share a weight panel (all m-tiles of an
+  // expert, its ragged tail included) run at the same time and share it in
+  // L2, while neighbouring column tiles share the token rows.  Each XCD walks
+  // a contiguous range of this order.
   const int mt_r = a.tile_off[a.E];
   const int mt_s = a.tile_off[a.E + 1] - mt_r;
   const int64_t tiles_r = (int64_t)mt_r * a.nt_r;
@@ -195,44 +248,60 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
   bool shared;
   int g, nt, K, N, valid;
   int64_t rb;  // first row of this tile in the group's row space
+  int mt, mt_g, ntiles, gm;
+  int64_t q;   // index of the tile inside its group
   if (tile < tiles_r) {
     shared = false;
-    const int mt = (int)(tile / a.nt_r);
-    nt = (int)(tile % a.nt_r);
-    int lo = 0, hi = a.E - 1;  // largest g with tile_off[g] <= mt
+    const int key = (int)(tile / a.nt_r);  // expert g owns keys tile_off[g] .. tile_off[g+1]-1
+    int lo = 0, hi = a.E - 1;              // largest g with tile_off[g] <= key
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (a.tile_off[mid] <= mt) lo = mid; else hi = mid - 1;
+      if (a.tile_off[mid] <= key) lo = mid; else hi = mid - 1;
     }
     g = lo;
-    const int m0 = (mt - a.tile_off[g]) * PF_BM;
-    valid = min(PF_BM, a.offsets[g + 1] - a.offsets[g] - m0);
-    rb = (int64_t)a.offsets[g] + m0;
+    q = tile - (int64_t)a.nt_r * a.tile_off[g];
+    mt_g = a.tile_off[g + 1] - a.tile_off[g];
+    ntiles = a.nt_r;
+    gm = PF_GM;
     K = a.K;
     N = a.N;
   } else {
     shared = true;
-    const int64_t ts = tile - tiles_r;
-    const int mt = (int)(ts / a.nt_s);
-    nt = (int)(ts % a.nt_s);
     g = a.E;
-    rb = (int64_t)mt * PF_BM;
-    valid = (int)min((int64_t)PF_BM, a.T - rb);
+    q = tile - tiles_r;
+    mt_g = mt_s;
+    ntiles = a.nt_s;
+    gm = PF_GM_SH;
     K = a.K_sh;
     N = a.N_sh;
+  }
+  {
+    const int64_t blk = q / ((int64_t)gm * ntiles);       // full blocks of gm m-tiles before
+    const int in_blk = (int)(q - blk * gm * ntiles);
+    const int bsize = min(gm, mt_g - (int)blk * gm);       // m-tiles in this block
+    nt = in_blk / bsize;
+    mt = (int)blk * gm + in_blk % bsize;
+  }
+  if (!shared) {
+    const int m0 = mt * PF_BM;
+    valid = min(PF_BM, a.offsets[g + 1] - a.offsets[g] - m0);
+    rb = (int64_t)a.offsets[g] + m0;
+  } else {
+    rb = (int64_t)mt * PF_BM;
+    valid = (int)min((int64_t)PF_BM, a.T - rb);
   }
   const int mtv = (valid + 31) >> 5;  // 32-row sub-tiles holding rows of this group
 
   // ---- DMA sources: lane l of wave w fetches, for q < 8, row 64w + 8q + l/8,
-  // chunk (l%8) ^ (l/8) of each operand
+  // chunk (l%8) ^ swz(row) = (l%8) ^ ((l/8) ^ q) of each operand
   const int lrow = 64 * wv + (lane >> 3);
-  const int lchunk = (lane & 7) ^ ((lane >> 3) & 7);
   const uint16_t *ap[PF_LOADS];
   const uint16_t *bp[PF_LOADS];
   const uint16_t *Abase = shared ? a.A_sh : a.A;
 #pragma unroll
   for (int q = 0; q < PF_LOADS; ++q) {
     const int row = lrow + 8 * q;
+    const int lchunk = (lane & 7) ^ swz(row);
     const int r = min(row, valid - 1);  // clamped: rows past the group are never stored
     const int64_t arow = (GATEUP && !shared) ? (int64_t)a.row_token[rb + r] : rb + r;
     ap[q] = Abase + arow * K + lchunk * 8;
@@ -260,16 +329,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
     acc[i][1] = f32x16_t{};
   }
 
-  switch (mtv) {  // branch-free main loop per count of valid 32-row sub-tiles
-    case 8: k_loop<8>(ap, bp, brow0, brow1, K, acc); break;
-    case 7: k_loop<7>(ap, bp, brow0, brow1, K, acc); break;
-    case 6: k_loop<6>(ap, bp, brow0, brow1, K, acc); break;
-    case 5: k_loop<5>(ap, bp, brow0, brow1, K, acc); break;
-    case 4: k_loop<4>(ap, bp, brow0, brow1, K, acc); break;
-    case 3: k_loop<3>(ap, bp, brow0, brow1, K, acc); break;
-    case 2: k_loop<2>(ap, bp, brow0, brow1, K, acc); break;
-    default: k_loop<1>(ap, bp, brow0, brow1, K, acc); break;
-  }
+  // branch-free main loop per count of valid 32-row sub-tiles, rounded up to
+  // one of 1, 2, 4, 6, 8 (the extra sub-tiles multiply rows that are never stored)
+  if (mtv > 6) k_loop<8>(ap, bp, brow0, brow1, K, acc);
+  else if (mtv > 4) k_loop<6>(ap, bp, brow0, brow1, K, acc);
+  else if (mtv > 2) k_loop<4>(ap, bp, brow0, brow1, K, acc);
+  else if (mtv > 1) k_loop<2>(ap, bp, brow0, brow1, K, acc);
+  else k_loop<1>(ap, bp, brow0, brow1, K, acc);
 
   // ---- epilogue; 32x32 D layout: lane holds rows 8*(r/4) + 4*(lane/32) + r%4 of column lane%32
   const int col = lane & 31;
