@@ -16,7 +16,7 @@
 //     |L - l| <= (d + 2) * 2^-52 * ||u_t|| ||c_e|| + 2^-50 |L| + d 2^-120.
 #include "common.h"
 
-#define ROUTER_CHUNK 256
+#define ROUTER_CHUNK 64
 #define RT_BM 64
 #define RT_BN 64
 #define RT_BK 64

@@ -12,7 +12,8 @@
 // L_e + B_e >= m can hold the maximum.  When that set has one member it is the
 // winner.  Otherwise its members' logits are recomputed in fp64 (exact
 // products, fp64 sums; bound ~(d/64 + 8) 2^-52 ||u|| ||c||) and written back in
-// place with their tighter bounds, and the round is re-decided.  Members whose
+// place with their tighter bounds, and the round is re-decided.  Members are
+// visited lowest index first by a wave-wide minimum.  Members whose
 // fp64 intervals still overlap are compared exactly: each key becomes a 256-bit
 // fixed-point sum of its exact products (bf16 x bf16 and fp32 x fp32 products
 // are exact in fp64) and the largest wins, ties to the lower index.  A product
@@ -103,15 +104,47 @@ __device__ void exact_key(const void *urow, const void *w, const float *bias, in
   for (int q = 0; q < EXACT_LIMBS; ++q) key[q] = wave_sum_i64(key[q]);
 }
 
-// Wave-cooperative fp64 logit of expert e (uniform result): exact products, fp64 sums.
+// Wave-cooperative fp64 logit of expert e (uniform result): exact products,
+// fp64 sums.  16-byte loads: lane l takes the 8 (bf16) or 4 (fp32) elements
+// of chunk l, l + 64, ... (d is a multiple of 64).
 template <bool BF16>
 __device__ double dot_f64(const void *urow, const void *w, const float *bias, int e, int d) {
   const int lane = threadIdx.x & 63;
   double acc = 0.0;
-  for (int i = lane; i < d; i += 64) acc = fma(load_elem<BF16>(urow, i), load_elem<BF16>(w, (int64_t)e * d + i), acc);
+  if (BF16) {
+    const uint4 *up = (const uint4 *)urow;
+    const uint4 *wp = (const uint4 *)((const uint16_t *)w + (int64_t)e * d);
+    for (int c = lane; c < d / 8; c += 64) {
+      const uint4 a = up[c], b = wp[c];
+      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc = fma((double)__uint_as_float(av[q] << 16), (double)__uint_as_float(bv[q] << 16), acc);
+        acc = fma((double)__uint_as_float(av[q] & 0xffff0000u), (double)__uint_as_float(bv[q] & 0xffff0000u), acc);
+      }
+    }
+  } else {
+    const float4 *up = (const float4 *)urow;
+    const float4 *wp = (const float4 *)((const float *)w + (int64_t)e * d);
+    for (int c = lane; c < d / 4; c += 64) {
+      const float4 a = up[c], b = wp[c];
+      acc = fma((double)a.x, (double)b.x, acc);
+      acc = fma((double)a.y, (double)b.y, acc);
+      acc = fma((double)a.z, (double)b.z, acc);
+      acc = fma((double)a.w, (double)b.w, acc);
+    }
+  }
   acc = wave_sum_f64(acc);
   if (bias) acc += (double)bias[e];
   return acc;
+}
+
+// Lowest expert index among the set bits of `bits` (bit s of lane l = expert
+// l + 64 s) over the wave, or a large value when no bit is set.
+__device__ __forceinline__ int lowest_expert(unsigned bits) {
+  const int lane = threadIdx.x & 63;
+  const int my = bits ? lane + 64 * (__ffs(bits) - 1) : 0x7fffffff;
+  return wave_min_i32(my);
 }
 
 template <int S, bool BF16>
@@ -179,14 +212,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
         break;
       }
       token_exact = true;
-      const unsigned need = member & ~refined;
+      unsigned need = member & ~refined;
       if (wave_sum_i32(__popc(need)) > 0) {
-        // level 2: fp64 logits of the unrefined members, written back in place.
-        // Members are visited by a uniform walk over all experts (expert e
-        // lives in lane e % 64, register slot e / 64).
-        for (int e = 0; e < E; ++e) {
-          const unsigned nb = (unsigned)__shfl((int)need, e & 63, 64);
-          if (!((nb >> (e >> 6)) & 1u)) continue;
+        // level 2: fp64 logits of the unrefined members, written back in place
+        // (expert e lives in lane e % 64, register slot e / 64)
+        for (int e = lowest_expert(need); e != 0x7fffffff; e = lowest_expert(need)) {
           const double l64 = dot_f64<BF16>(urow, w, bias, e, d);
           const double b64 = c64 * sqrt(unorm * wn2[e]) * (1.0 + 0x1p-30) + 0x1p-51 * fabs(l64) + d * 0x1p-120;
 #pragma unroll
@@ -195,6 +225,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
               L[s] = l64;
               B[s] = b64;
               refined |= 1u << s;
+              need &= ~(1u << s);
             }
         }
         if (lane == 0) atomicAdd(&diag->refinements, 1u);
@@ -207,11 +238,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
         eu = wave_max_i32(m);
       }
       int ew = -100000, eb = -100000;
-      for (int e = 0; e < E; ++e) {
-        const unsigned mb = (unsigned)__shfl((int)member, e & 63, 64);
-        if (!((mb >> (e >> 6)) & 1u)) continue;
+      for (unsigned rest = member; ; ) {
+        const int e = lowest_expert(rest);
+        if (e == 0x7fffffff) break;
         for (int i = lane; i < d; i += 64) ew = max(ew, exponent_of(load_elem<BF16>(w, (int64_t)e * d + i)));
         if (bias) eb = max(eb, exponent_of((double)bias[e]));
+        if ((e & 63) == lane) rest &= ~(1u << (e >> 6));
       }
       ew = wave_max_i32(ew);
       eb = __builtin_amdgcn_readfirstlane(eb);
@@ -224,9 +256,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
       int wn = -1;
 #pragma unroll
       for (int q = 0; q < EXACT_LIMBS; ++q) best[q] = 0;
-      for (int e = 0; e < E; ++e) {
-        const unsigned mb = (unsigned)__shfl((int)member, e & 63, 64);
-        if (!((mb >> (e >> 6)) & 1u)) continue;
+      for (unsigned rest = member; ; ) {  // ascending expert order
+        const int e = lowest_expert(rest);
+        if (e == 0x7fffffff) break;
+        if ((e & 63) == lane) rest &= ~(1u << (e >> 6));
         exact_key<BF16>(urow, w, bias, e, d, E0, cur, bad);
         // keys are wave sums: make their uniformity explicit before comparing
         int better = 0;
