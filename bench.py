@@ -11,6 +11,7 @@ weights.  The CPU oracle is timed on a bounded token slice as a baseline.
 """
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -22,6 +23,24 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12  # 2516.6: 256 CUs x 4096 FLOP/clk x 2.4 GHz (dense)
 PEAK_HBM_GBS = 8000.0
 STAGES = ["router_logits", "topk", "permute", "gate_up", "down", "combine"]
+CSRC = os.path.join(ROOT, "fine_grained_routed_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+
+
+def source_sha256(name: str) -> str:
+    return hashlib.sha256(open(os.path.join(CSRC, name), "rb").read()).hexdigest()
+
+
+def measured_traffic(key: str, source: str):
+    """HBM bytes per dispatch from the committed counter summary, or None when the
+    kernel source has changed since the counters were taken (or none were)."""
+    try:
+        kv = dict(l.strip().split("=", 1) for l in open(TRAFFIC_FILE) if "=" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    if kv.get(f"{key}_source_sha256") != source_sha256(source) or not kv.get(f"{key}_bytes"):
+        return None
+    return float(kv[f"{key}_bytes"])
 
 
 class HipEvents:
@@ -159,7 +178,9 @@ def main():
                    "n_shared": wl.n_shared, "top_k": wl.top_k},
         "roofline": {"bound": "mfma", "kernel": "grouped_gemm_bf16_kernel<gate_up>",
                      "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gu_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": gu_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic("gate_up_prefill", "ffn_prefill.hip"),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         "layer_tflops": total_flop / (wall_ms * 1e-3) / 1e12,
         "layer_frac_of_peak": total_flop / (wall_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stage_ms": stage,
@@ -186,7 +207,8 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "gate_up (decode path)",
                          "achieved": gu_bytes / (d_stage["gate_up"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": gu_bytes / (d_stage["gate_up"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "traffic": None},
+                         "traffic": measured_traffic("gate_up_decode", "ffn_decode.hip"),
+                         "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         }
 
     if not args.no_cpu_baseline:
