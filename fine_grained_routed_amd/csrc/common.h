@@ -9,7 +9,6 @@
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 #define MOE_WAVE 64
 
@@ -28,12 +27,6 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   union { uint4 u; bf16x8_t b; } c;
   c.u = v;
   return c.b;
-}
-
-// 16-byte load that bypasses cache retention (streamed data read once)
-__device__ __forceinline__ uint4 load_stream16(const void *p) {
-  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t *)p);
-  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // keep v when ok, else zeros (component-wise, so it stays in registers)

@@ -11,11 +11,12 @@
 // experts that received no token have no tile and cost nothing.  Each of the
 // 4 waves of a work-group owns 32 output columns and walks the whole reduction
 // depth, loading the weight fragments of 16x16x32 matrix-core steps straight
-// from HBM into registers with non-temporal loads (no LDS: each weight
-// element is used by this wave only); the 16 token rows are re-read from L2.
+// from HBM into registers (no LDS: each weight element is used by this wave
+// only); the 16 token rows are re-read from L2.
 // An expert's weights are streamed once per 16 of its rows (once for nearly
 // every expert at decode sizes; the tiles of one expert run together, so
-// repeats mostly hit L2).  Loads are issued DK_UNROLL steps ahead of use.
+// repeats mostly hit L2).  Each wave issues the loads of DK_UNROLL steps
+// before their MFMAs.
 //
 // gate/up: H[r, n] = SiLU(A[r,:] . W1_g[n,:]) * (A[r,:] . W3_g[n,:]), bf16 out
 // down:    Y[r, n] = H[r,:] . W2_g[n,:], fp32 out
@@ -44,6 +45,12 @@ struct DecodeArgs {
 };
 
 __device__ __forceinline__ float dk_silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// Weight loads are ordinary (cached) loads: each 128-byte line of a weight row
+// is requested as two 64-byte halves by two instructions, and with
+// non-temporal loads the second half often misses L2 again (measured: 1.7x
+// the weight bytes fetched from memory); cached, it hits.
+__device__ __forceinline__ uint4 dk_load(const uint16_t *p) { return *(const uint4 *)p; }
 
 template <bool GATEUP>
 __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeArgs a) {
@@ -118,8 +125,8 @@ __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeArgs a) {
       av[s] = *(const uint4 *)(ap + k0 + 32 * s);
 #pragma unroll
       for (int j = 0; j < DK_NT; ++j) {
-        b1[s][j] = load_stream16(p1[j] + k0 + 32 * s);
-        if (GATEUP) b3[s][j] = load_stream16(p3[j] + k0 + 32 * s);
+        b1[s][j] = dk_load(p1[j] + k0 + 32 * s);
+        if (GATEUP) b3[s][j] = dk_load(p3[j] + k0 + 32 * s);
       }
     }
 #pragma unroll
@@ -131,14 +138,18 @@ __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeArgs a) {
         if (GATEUP) acc3[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(b3[s][j]), acc3[j], 0, 0, 0);
       }
     }
+    // keep every load of the batch ahead of its MFMAs (the scheduler would
+    // otherwise interleave them and hold only a few loads in flight)
+    __builtin_amdgcn_sched_group_barrier(0x020, DK_UNROLL * (1 + DK_NT * (GATEUP ? 2 : 1)), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, DK_UNROLL * DK_NT * (GATEUP ? 2 : 1), 0);
   }
   for (int k0 = kmain; k0 < K; k0 += 32) {
     const bf16x8_t a8 = as_bf16x8(*(const uint4 *)(ap + k0));
 #pragma unroll
     for (int j = 0; j < DK_NT; ++j) {
-      acc1[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(load_stream16(p1[j] + k0)), acc1[j], 0, 0, 0);
+      acc1[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(dk_load(p1[j] + k0)), acc1[j], 0, 0, 0);
       if (GATEUP)
-        acc3[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(load_stream16(p3[j] + k0)), acc3[j], 0, 0, 0);
+        acc3[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(dk_load(p3[j] + k0)), acc3[j], 0, 0, 0);
     }
   }
   // ---- epilogue: lane holds rows 4*(lane/16)+q of column lane%16 of each tile
