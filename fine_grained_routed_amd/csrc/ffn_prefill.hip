@@ -16,10 +16,13 @@
 //
 // Tiles: up to 256 rows x 256 B-columns x 64 deep per work-group; B-columns
 // are 128 gate + the same 128 up columns (gate/up) or 256 output columns
-// (down).  4 waves split the columns (1 x 4): each wave owns all 256 rows and
-// 64 B-columns as 8 x 2 tiles of the 32x32x16 bf16 matrix-core instruction,
-// 256 fp32 accumulators per lane.  A wave skips the 32-row sub-tiles past the
-// group's last row, so a ragged tail costs in proportion to its rows.  Both
+// (down).  4 waves in a 2 x 2 layout: each wave owns 128 rows and 128
+// B-columns (gate/up: 64 gate + the matching 64 up columns) as 4 x 4 tiles
+// of the 32x32x16 bf16 matrix-core instruction, 256 fp32 accumulators per
+// lane; per 16-deep step a wave reads 8 fragments from LDS for 16
+// instructions, and issues the next step's 8 reads under the first 8 of them.
+// A wave skips the 32-row sub-tiles past the group's last row, so a ragged
+// tail costs in proportion to its rows.  Both
 // operands are K-contiguous; LDS rows of 64 bf16 hold their 16-byte chunks
 // XOR-swizzled per row so that fragment reads are free of bank conflicts.
 // LDS is filled by direct global-to-LDS loads (global_load_lds_dwordx4: each
@@ -47,7 +50,7 @@
 #define PF_BN 256    // B rows per tile (gate/up: 128 gate + 128 up)
 #define PF_BK 64
 #define PF_BM_IDX 4  // moe_bm_of(4) == 256
-#define PF_MT 8      // 32-row sub-tiles per tile
+#define PF_WM 4      // 32-row sub-tiles per wave (2 x 2 waves over 8 sub-tiles)
 #define PF_GM 8      // m-tiles per ordering block (routed experts)
 #define PF_GM_SH 4   // m-tiles per ordering block (shared group)
 #define PF_LOADS 8   // DMA instructions per wave per operand per k-tile (8 rows of 128 B each)
@@ -62,6 +65,7 @@ struct GemmArgs {
   const uint16_t *B1s, *B3s; // shared
   void *C, *C_sh;            // gate/up: H bf16 [R, f], H_sh [T, f_s]; down: Y f32 [R, d], Y_sh [T, d]
   int64_t T;
+  int64_t rows_a, rows_a_sh;  // rows of A and A_sh (bounds of their buffer resources)
   int E, K, K_sh, N, N_sh, has_shared;
   int nt_r, nt_s;            // column tiles of a routed / the shared group
 };
@@ -80,22 +84,29 @@ __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 // element offset of 16-byte chunk c of LDS row r
 __device__ __forceinline__ int lds_off(int r, int c) { return r * PF_BK + ((c ^ swz(r)) << 3); }
 
-// 16 bytes per lane from global memory straight into LDS at dst + 16 * lane
-__device__ __forceinline__ void dma16(const uint16_t *src, uint16_t *dst) {
-  __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_t *)dst, 16, 0, 0);
+// Buffer resource over `bytes` bytes at `base` (raw buffer: no stride, 32-bit
+// data format), the form the buffer-to-LDS loads address memory through.
+// Accesses past `bytes` read zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                           (int)(uint32_t)min(bytes, (uint64_t)0xffffffffu), 0x00020000);
 }
 
+// s_waitcnt immediate (gfx9 layout: vmcnt [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]) for "at most vm vector-memory operations outstanding, LDS
+// and scalar loads complete".  The builtin, unlike inline asm, is visible to
+// the compiler's own wait tracking, which then knows that older DMA into a
+// stage has landed.
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+
 // Publish LDS to the work-group: this wave's LDS reads are complete and at
-// most one k-tile of B DMA (8 instructions) is still in flight, then the
-// work-group barrier.  Written out rather than __syncthreads(), whose release
-// fence would also wait for every DMA in flight and so drain the prefetch.
+// most `vm` DMA instructions are still in flight, then the work-group barrier.
+// Written out rather than __syncthreads(), whose release fence would also
+// wait for every DMA in flight and so drain the prefetch.
+template <int VM>
 __device__ __forceinline__ void publish() {
-  // s_waitcnt immediate (gfx9 layout: vmcnt [3:0] and [15:14], expcnt [6:4],
-  // lgkmcnt [11:8]): vmcnt 8, expcnt 7, lgkmcnt 0.  The builtin, unlike
-  // inline asm, is visible to the compiler's own wait tracking, which then
-  // knows that older DMA into a stage has landed.
   asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x0078);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM));
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -114,115 +125,180 @@ __device__ __forceinline__ uint16_t *stage_a() { return SA == 0 ? g_As0 : g_As1;
 template <int SB>
 __device__ __forceinline__ uint16_t *stage_b() { return SB == 0 ? g_Bs0 : SB == 1 ? g_Bs1 : g_Bs2; }
 
-// DMA of one operand's k-tile at k0.  Wave w fills LDS rows 64w + 8q ..
-// 64w + 8q + 7 (q < 8); lane l writes row 64w + 8q + l/8, slot l%8, which
-// holds global chunk (l%8) ^ swz(row) (the per-q chunk is folded into src[q]).
-__device__ __forceinline__ void issue_op(const uint16_t *const (&src)[PF_LOADS], uint16_t *stage, int k0) {
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int q = 0; q < PF_LOADS; ++q) dma16(src[q] + k0, stage + (64 * wv + 8 * q) * PF_BK);
-}
-
-// Fragments of one 16-deep step: two B column tiles and MTV A row tiles.
-template <int MTV>
-struct Frags {
-  bf16x8_t b0, b1, a[MTV];
+// One operand's DMA sources: a buffer resource over the matrix the wave's
+// rows come from and each lane's byte offset for its 8 row segments.
+struct Operand {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off[PF_LOADS];
 };
 
-template <int MTV, int SA, int SB>
-__device__ __forceinline__ void read_frags(Frags<MTV> &f, int brow0, int brow1, int step) {
+// DMA of one operand's k-tile kt, 16 bytes per lane straight from memory into
+// LDS at stage row 64w + 8q (lane l lands at +16 l): wave w fills LDS rows
+// 64w + 8q .. 64w + 8q + 7 (q < 8); lane l writes row 64w + 8q + l/8, slot
+// l%8, which holds global chunk (l%8) ^ swz(row) (folded into the offsets).
+// The k-tile's position is the scalar offset, so advancing costs one add.
+template <int Q0 = 0, int Q1 = PF_LOADS>
+__device__ __forceinline__ void issue_op(const Operand &op, uint16_t *stage, int kt) {
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int koff = kt * (PF_BK * 2);
+#pragma unroll
+  for (int q = Q0; q < Q1; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (lds_void_t *)(stage + (64 * wv + 8 * q) * PF_BK), 16,
+                                             (int)op.off[q], koff, 0, 0);
+}
+
+// Fragments of one 16-deep step: MW A row tiles and four B column tiles.
+template <int MW>
+struct Frags {
+  bf16x8_t a[PF_WM], b[4];
+};
+
+// Fragment rows of the wave's tiles inside the LDS stages.
+struct WaveRows {
+  int a0;     // first A row of the wave (0 or 128)
+  int b[4];   // first B row of each column tile
+};
+
+// Reads in the order the next step consumes them: a0, the four B tiles, a1..
+template <int MW, int SA, int SB>
+__device__ __forceinline__ void read_frags(Frags<MW> &f, const WaveRows &w, int step) {
   const uint16_t *As = stage_a<SA>();
   const uint16_t *Bs = stage_b<SB>();
   const int lane = threadIdx.x & 63;
   const int frow = lane & 31;             // fragment row inside a 32-row tile
   const int ch = step * 2 + (lane >> 5);  // chunk: first/second 8 of the 16-deep step
-  f.b0 = as_bf16x8(*(const uint4 *)&Bs[lds_off(brow0 + frow, ch)]);
-  f.b1 = as_bf16x8(*(const uint4 *)&Bs[lds_off(brow1 + frow, ch)]);
+  if (MW > 0) f.a[0] = as_bf16x8(*(const uint4 *)&As[lds_off(w.a0 + frow, ch)]);
 #pragma unroll
-  for (int i = 0; i < MTV; ++i) f.a[i] = as_bf16x8(*(const uint4 *)&As[lds_off(i * 32 + frow, ch)]);
+  for (int j = 0; j < 4; ++j) f.b[j] = as_bf16x8(*(const uint4 *)&Bs[lds_off(w.b[j] + frow, ch)]);
+#pragma unroll
+  for (int i = 1; i < MW; ++i) f.a[i] = as_bf16x8(*(const uint4 *)&As[lds_off(w.a0 + i * 32 + frow, ch)]);
 }
 
-template <int MTV>
-__device__ __forceinline__ void mfma_step(const Frags<MTV> &f, f32x16_t (&acc)[PF_MT][2]) {
+// The weight fragment is the first operand, so each accumulator holds the
+// transposed product: a lane owns one token row (lane % 32) and, per group of
+// four registers, four consecutive output columns, which the epilogue stores
+// as one vector.
+template <int MW>
+__device__ __forceinline__ void mfma_step(const Frags<MW> &f, f32x16_t (&acc)[PF_WM][4]) {
 #pragma unroll
-  for (int i = 0; i < MTV; ++i) {
-    acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b0, acc[i][0], 0, 0, 0);
-    acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b1, acc[i][1], 0, 0, 0);
-  }
+  for (int i = 0; i < MW; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
-// MFMAs of one step in pairs, each pair followed by one fragment read of the next step
-template <int MTV>
+// One fragment read after each of the step's first MFMAs, so that every read
+// of the next step is issued early and has the remaining MFMAs to land; the
+// step's share of weight-tile DMA (ND instructions) goes under the rest.
+template <int MW, int ND>
 __device__ __forceinline__ void interleave_hint() {
+  constexpr int nm = 4 * MW, nr = MW > 0 ? 4 + MW : 0;
 #pragma unroll
-  for (int i = 0; i < MTV; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  for (int t = 0; t < nr; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int t = 0; t < ND; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+  if (nm > nr + ND) __builtin_amdgcn_sched_group_barrier(0x008, nm - nr - ND, 0);
+}
+
+// MFMAs of step 3 after the barrier: the step-0 fragment reads of the next
+// tile go under the first MFMAs, the token-tile DMA under the rest.
+template <int MW>
+__device__ __forceinline__ void post_barrier_hint() {
+  constexpr int nm = 4 * MW, nr = MW > 0 ? 4 + MW : 0;
+#pragma unroll
+  for (int t = 0; t < nr; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int t = nr; t < nm; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
 }
 
 // One k-tile j, its token rows in A-stage SA (= j % 2) and weights in B-stage
 // SB (= j % 3).  f0 holds its step-0 fragments on entry and the next tile's
-// step-0 fragments on exit.  Every iteration issues exactly one A tile (j + 1)
-// and one B tile (j + 2) of DMA, past the end re-fetching the last tile into
-// a stage nobody reads again, so the count of DMA in flight is the same on
-// every path and one constant wait publishes tile j + 1.
-template <int MTV, int SA, int SB>
-__device__ __forceinline__ void k_iter(const uint16_t *const (&ap)[PF_LOADS], const uint16_t *const (&bp)[PF_LOADS],
-                                       int brow0, int brow1, int j, int nk, Frags<MTV> &f0, Frags<MTV> &f1,
-                                       f32x16_t (&acc)[PF_MT][2]) {
-  // stages of tile j - 1 (read completely before the previous barrier)
-  issue_op(ap, stage_a<SA ^ 1>(), min(j + 1, nk - 1) * PF_BK);
-  issue_op(bp, stage_b<(SB + 2) % 3>(), min(j + 2, nk - 1) * PF_BK);
-  read_frags<MTV, SA, SB>(f1, brow0, brow1, 1);
-  mfma_step<MTV>(f0, acc);
-  interleave_hint<MTV>();
-  read_frags<MTV, SA, SB>(f0, brow0, brow1, 2);
-  mfma_step<MTV>(f1, acc);
-  interleave_hint<MTV>();
-  read_frags<MTV, SA, SB>(f1, brow0, brow1, 3);
-  mfma_step<MTV>(f0, acc);
-  interleave_hint<MTV>();
-  // publish tile j + 1 (A issued last iteration... this one; B two iterations ago)
-  publish();
+// step-0 fragments on exit.  DMA is spread over the iteration so that the
+// memory pipeline never holds a burst: the weight tile j + 2 goes into the
+// B stage of tile j - 1 under steps 0-2 (3 + 3 + 2 instructions), and after
+// the barrier that publishes tile j + 1 the token tile j + 2 goes into the A
+// stage of tile j, now free.  Past the end the last tile is re-fetched into
+// stages nobody reads again, so every iteration issues the same DMA and one
+// constant wait publishes the next tile: when it runs, only the weight tile
+// issued in this iteration may be in flight.
+template <int MW, int SA, int SB>
+__device__ __forceinline__ void k_iter(const Operand &A, const Operand &B, const WaveRows &w, int j, int nk,
+                                       Frags<MW> &f0, Frags<MW> &f1, f32x16_t (&acc)[PF_WM][4]) {
+  const int kb = min(j + 2, nk - 1);
+  if (MW > 0) read_frags<MW, SA, SB>(f1, w, 1);
+  issue_op<0, 3>(B, stage_b<(SB + 2) % 3>(), kb);
+  if (MW > 0) {
+    mfma_step<MW>(f0, acc);
+    interleave_hint<MW, 3>();
+    read_frags<MW, SA, SB>(f0, w, 2);
+  }
+  issue_op<3, 6>(B, stage_b<(SB + 2) % 3>(), kb);
+  if (MW > 0) {
+    mfma_step<MW>(f1, acc);
+    interleave_hint<MW, 3>();
+    read_frags<MW, SA, SB>(f1, w, 3);
+  }
+  issue_op<6, 8>(B, stage_b<(SB + 2) % 3>(), kb);
+  if (MW > 0) {
+    mfma_step<MW>(f0, acc);
+    interleave_hint<MW, 2>();
+  }
+  publish<PF_LOADS>();  // A and B tiles j + 1 landed
   // step-0 fragments of tile j + 1 (after the last tile this reads stages
   // whose values are never used; reading LDS is always in bounds)
-  read_frags<MTV, SA ^ 1, (SB + 1) % 3>(f0, brow0, brow1, 0);
-  mfma_step<MTV>(f1, acc);
-  interleave_hint<MTV>();
+  if (MW > 0) read_frags<MW, SA ^ 1, (SB + 1) % 3>(f0, w, 0);
+  issue_op(A, stage_a<SA>(), min(j + 2, nk - 1));
+  if (MW > 0) {
+    mfma_step<MW>(f1, acc);
+    post_barrier_hint<MW>();
+  }
 }
 
-// The k loop of one tile with MTV valid 32-row sub-tiles (compile-time, so
-// the body is straight-line).
-template <int MTV>
-__device__ __forceinline__ void k_loop(const uint16_t *const (&ap)[PF_LOADS], const uint16_t *const (&bp)[PF_LOADS],
-                                       int brow0, int brow1, int K, f32x16_t (&acc)[PF_MT][2]) {
+// The k loop of one tile for a wave with MW valid 32-row sub-tiles
+// (compile-time, so the body is straight-line).  Every wave of the
+// work-group, whatever its MW, issues the same DMA and barriers.
+template <int MW>
+__device__ __forceinline__ void k_loop(const Operand &A, const Operand &B, const WaveRows &w, int K,
+                                       f32x16_t (&acc)[PF_WM][4]) {
   const int nk = K / PF_BK;
-  issue_op(ap, stage_a<0>(), 0);
-  issue_op(bp, stage_b<0>(), 0);
-  issue_op(bp, stage_b<1>(), min(1, nk - 1) * PF_BK);
-  publish();  // tile 0 landed; B tile 1 may be in flight
-  Frags<MTV> f0, f1;
-  read_frags<MTV, 0, 0>(f0, brow0, brow1, 0);
+  // prologue: A tiles 0, 1 and B tiles 0, 1 (clamped), issued in the order the
+  // loop's constant wait assumes
+  issue_op(A, stage_a<0>(), 0);
+  issue_op(B, stage_b<0>(), 0);
+  issue_op(B, stage_b<1>(), min(1, nk - 1));
+  issue_op(A, stage_a<1>(), min(1, nk - 1));
+  publish<2 * PF_LOADS>();  // A0 and B0 landed
+  Frags<MW> f0, f1;
+  if (MW > 0) read_frags<MW, 0, 0>(f0, w, 0);
   // six k-tiles per trip (the stage pattern repeats every lcm(2, 3) tiles);
   // whole trips are unconditional, the remainder follows
   int j = 0;
   for (; j + 6 <= nk; j += 6) {
-    k_iter<MTV, 0, 0>(ap, bp, brow0, brow1, j, nk, f0, f1, acc);
-    k_iter<MTV, 1, 1>(ap, bp, brow0, brow1, j + 1, nk, f0, f1, acc);
-    k_iter<MTV, 0, 2>(ap, bp, brow0, brow1, j + 2, nk, f0, f1, acc);
-    k_iter<MTV, 1, 0>(ap, bp, brow0, brow1, j + 3, nk, f0, f1, acc);
-    k_iter<MTV, 0, 1>(ap, bp, brow0, brow1, j + 4, nk, f0, f1, acc);
-    k_iter<MTV, 1, 2>(ap, bp, brow0, brow1, j + 5, nk, f0, f1, acc);
+    k_iter<MW, 0, 0>(A, B, w, j, nk, f0, f1, acc);
+    k_iter<MW, 1, 1>(A, B, w, j + 1, nk, f0, f1, acc);
+    k_iter<MW, 0, 2>(A, B, w, j + 2, nk, f0, f1, acc);
+    k_iter<MW, 1, 0>(A, B, w, j + 3, nk, f0, f1, acc);
+    k_iter<MW, 0, 1>(A, B, w, j + 4, nk, f0, f1, acc);
+    k_iter<MW, 1, 2>(A, B, w, j + 5, nk, f0, f1, acc);
   }
-  if (j < nk) k_iter<MTV, 0, 0>(ap, bp, brow0, brow1, j, nk, f0, f1, acc);
-  if (j + 1 < nk) k_iter<MTV, 1, 1>(ap, bp, brow0, brow1, j + 1, nk, f0, f1, acc);
-  if (j + 2 < nk) k_iter<MTV, 0, 2>(ap, bp, brow0, brow1, j + 2, nk, f0, f1, acc);
-  if (j + 3 < nk) k_iter<MTV, 1, 0>(ap, bp, brow0, brow1, j + 3, nk, f0, f1, acc);
-  if (j + 4 < nk) k_iter<MTV, 0, 1>(ap, bp, brow0, brow1, j + 4, nk, f0, f1, acc);
+  if (j < nk) k_iter<MW, 0, 0>(A, B, w, j, nk, f0, f1, acc);
+  if (j + 1 < nk) k_iter<MW, 1, 1>(A, B, w, j + 1, nk, f0, f1, acc);
+  if (j + 2 < nk) k_iter<MW, 0, 2>(A, B, w, j + 2, nk, f0, f1, acc);
+  if (j + 3 < nk) k_iter<MW, 1, 0>(A, B, w, j + 3, nk, f0, f1, acc);
+  if (j + 4 < nk) k_iter<MW, 0, 1>(A, B, w, j + 4, nk, f0, f1, acc);
   // the trailing re-fetches must land before the work-group can exit
-  __builtin_amdgcn_s_waitcnt(0x0070);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
 template <bool GATEUP>
@@ -290,83 +366,101 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
     rb = (int64_t)mt * PF_BM;
     valid = (int)min((int64_t)PF_BM, a.T - rb);
   }
-  const int mtv = (valid + 31) >> 5;  // 32-row sub-tiles holding rows of this group
+  const int wm = wv >> 1, wn = wv & 1;  // 2 x 2 wave layout
+  // 32-row sub-tiles of this wave's 128 rows that hold rows of the group
+  const int mw = min(PF_WM, max(0, ((valid + 31) >> 5) - PF_WM * wm));
 
   // ---- DMA sources: lane l of wave w fetches, for q < 8, row 64w + 8q + l/8,
-  // chunk (l%8) ^ swz(row) = (l%8) ^ ((l/8) ^ q) of each operand
+  // chunk (l%8) ^ swz(row) = (l%8) ^ ((l/8) ^ q) of each operand.  Byte
+  // offsets fit in 32 bits (the host checks the operand sizes).
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
   const int lrow = 64 * wv + (lane >> 3);
-  const uint16_t *ap[PF_LOADS];
-  const uint16_t *bp[PF_LOADS];
-  const uint16_t *Abase = shared ? a.A_sh : a.A;
+  Operand A, B;
+  A.rsrc = shared ? make_rsrc(a.A_sh, (uint64_t)a.rows_a_sh * K * 2) : make_rsrc(a.A, (uint64_t)a.rows_a * K * 2);
+  {
+    const uint64_t wbytes = (uint64_t)N * K * 2;  // one expert's matrix
+    const uint16_t *bw;
+    if (GATEUP) {
+      // waves 0, 1 fetch gate rows (W1), waves 2, 3 the same rows of up (W3)
+      const bool up = wvu >= 2;
+      bw = shared ? (up ? a.B3s : a.B1s) : ((up ? a.B3 : a.B1) + (int64_t)g * N * K);
+    } else {
+      bw = shared ? a.B1s : (a.B1 + (int64_t)g * N * K);
+    }
+    B.rsrc = make_rsrc(bw, wbytes);
+  }
 #pragma unroll
   for (int q = 0; q < PF_LOADS; ++q) {
     const int row = lrow + 8 * q;
     const int lchunk = (lane & 7) ^ swz(row);
     const int r = min(row, valid - 1);  // clamped: rows past the group are never stored
     const int64_t arow = (GATEUP && !shared) ? (int64_t)a.row_token[rb + r] : rb + r;
-    ap[q] = Abase + arow * K + lchunk * 8;
-    int n;
-    const uint16_t *bw;
-    if (GATEUP) {
-      n = nt * (PF_BN / 2) + (row & (PF_BN / 2 - 1));
-      const bool up = row >= PF_BN / 2;
-      bw = shared ? (up ? a.B3s : a.B1s) : ((up ? a.B3 : a.B1) + (int64_t)g * N * K);
-    } else {
-      n = nt * PF_BN + row;
-      bw = shared ? a.B1s : (a.B1 + (int64_t)g * N * K);
-    }
-    bp[q] = bw + (int64_t)min(n, N - 1) * K + lchunk * 8;  // clamped: columns >= N are never stored
+    A.off[q] = (uint32_t)(arow * K * 2 + lchunk * 16);
+    const int n = GATEUP ? nt * (PF_BN / 2) + (row & (PF_BN / 2 - 1)) : nt * PF_BN + row;
+    B.off[q] = (uint32_t)((int64_t)min(n, N - 1) * K * 2 + lchunk * 16);  // clamped: columns >= N are never stored
   }
 
-  // B rows of the wave's two 32-column tiles
-  const int brow0 = GATEUP ? wv * 32 : wv * 64;
-  const int brow1 = GATEUP ? PF_BN / 2 + wv * 32 : wv * 64 + 32;
-
-  f32x16_t acc[PF_MT][2];
+  // LDS rows of the wave's A sub-tiles and B column tiles (gate/up: tiles 0, 1
+  // are gate columns, 2, 3 the same columns of up)
+  WaveRows w;
+  w.a0 = wm * (PF_BM / 2);
 #pragma unroll
-  for (int i = 0; i < PF_MT; ++i) {
-    acc[i][0] = f32x16_t{};
-    acc[i][1] = f32x16_t{};
-  }
+  for (int j = 0; j < 4; ++j)
+    w.b[j] = GATEUP ? (j >> 1) * (PF_BN / 2) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
 
-  // branch-free main loop per count of valid 32-row sub-tiles, rounded up to
-  // one of 1, 2, 4, 6, 8 (the extra sub-tiles multiply rows that are never stored)
-  if (mtv > 6) k_loop<8>(ap, bp, brow0, brow1, K, acc);
-  else if (mtv > 4) k_loop<6>(ap, bp, brow0, brow1, K, acc);
-  else if (mtv > 2) k_loop<4>(ap, bp, brow0, brow1, K, acc);
-  else if (mtv > 1) k_loop<2>(ap, bp, brow0, brow1, K, acc);
-  else k_loop<1>(ap, bp, brow0, brow1, K, acc);
+  f32x16_t acc[PF_WM][4];
+#pragma unroll
+  for (int i = 0; i < PF_WM; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-  // ---- epilogue; 32x32 D layout: lane holds rows 8*(r/4) + 4*(lane/32) + r%4 of column lane%32
-  const int col = lane & 31;
+  // branch-free main loop per count of valid sub-tiles of this wave
+  if (mw == 4) k_loop<4>(A, B, w, K, acc);
+  else if (mw == 3) k_loop<3>(A, B, w, K, acc);
+  else if (mw == 2) k_loop<2>(A, B, w, K, acc);
+  else if (mw == 1) k_loop<1>(A, B, w, K, acc);
+  else k_loop<0>(A, B, w, K, acc);
+
+  // ---- epilogue.  32x32 accumulator layout (transposed product): register
+  // 4q + c of lane l holds token row l % 32 of the sub-tile and output column
+  // 8q + 4 (l / 32) + c of the column tile.
+  const int mrow = lane & 31;
+  const int cgrp = 4 * (lane >> 5);
   if (GATEUP) {
     uint16_t *C = (uint16_t *)(shared ? a.C_sh : a.C);
-    const int n = nt * (PF_BN / 2) + wv * 32 + col;
-    if (n < N) {
 #pragma unroll
-      for (int i = 0; i < PF_MT; ++i) {
-        if (i >= mtv) continue;
+    for (int j = 0; j < 2; ++j) {
+      const int nb = nt * (PF_BN / 2) + wn * 64 + j * 32 + cgrp;
+      if (nb >= N) continue;  // N is a multiple of 64: a group of 4 is all in or all out
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (row < valid) C[(rb + row) * (int64_t)N + n] = f32_to_bf16(silu_f(acc[i][0][r]) * acc[i][1][r]);
+      for (int i = 0; i < PF_WM; ++i) {
+        const int row = w.a0 + i * 32 + mrow;
+        if (i >= mw || row >= valid) continue;
+        uint16_t *crow = C + (rb + row) * (int64_t)N + nb;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t h[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) h[c] = f32_to_bf16(silu_f(acc[i][j][4 * q + c]) * acc[i][j + 2][4 * q + c]);
+          *(uint2 *)(crow + 8 * q) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
         }
       }
     }
   } else {
     float *C = (float *)(shared ? a.C_sh : a.C);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = nt * PF_BN + wv * 64 + j * 32 + col;
-      if (n >= N) continue;
+    for (int j = 0; j < 4; ++j) {
+      const int nb = nt * PF_BN + wn * 128 + j * 32 + cgrp;
+      if (nb >= N) continue;
 #pragma unroll
-      for (int i = 0; i < PF_MT; ++i) {
-        if (i >= mtv) continue;
+      for (int i = 0; i < PF_WM; ++i) {
+        const int row = w.a0 + i * 32 + mrow;
+        if (i >= mw || row >= valid) continue;
+        float *crow = C + (rb + row) * (int64_t)N + nb;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (row < valid) C[(rb + row) * (int64_t)N + n] = acc[i][j][r];
-        }
+        for (int q = 0; q < 4; ++q)
+          *(float4 *)(crow + 8 * q) = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                                  acc[i][j][4 * q + 3]);
       }
     }
   }
@@ -399,6 +493,8 @@ hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u,
   g1.C = H;
   g1.C_sh = Hs;
   g1.T = T;
+  g1.rows_a = T;
+  g1.rows_a_sh = T;
   g1.E = E;
   g1.K = d;
   g1.K_sh = d;
@@ -423,6 +519,8 @@ hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u,
   g2.C = y_rows;
   g2.C_sh = y_sh;
   g2.T = T;
+  g2.rows_a = R;
+  g2.rows_a_sh = T;
   g2.E = E;
   g2.K = f;
   g2.K_sh = fs;
