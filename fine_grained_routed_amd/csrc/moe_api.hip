@@ -124,6 +124,21 @@ struct EventHook {
   }
 };
 
+// The bf16 prefill GEMMs address their operands through buffer resources
+// with 32-bit byte offsets: every matrix they read must stay under 4 GiB.
+static moe_status check_path_limits(const moe_dims &dm, int64_t T, const moe_options *o) {
+  if (dm.dtype != MOE_BF16 || pick_path(dm, T, o) != 1) return MOE_OK;
+  const uint64_t lim = (uint64_t)1 << 32;
+  const uint64_t R = (uint64_t)T * dm.top_k;
+  if ((uint64_t)T * dm.d_model * 2 >= lim || R * dm.d_ff * 2 >= lim || (uint64_t)T * dm.d_ff_shared * 2 >= lim ||
+      (uint64_t)dm.d_ff * dm.d_model * 2 >= lim || (uint64_t)dm.d_ff_shared * dm.d_model * 2 >= lim)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "prefill path: u [T, d], the hidden activations [T*k, f] / [T, f_s] and each weight matrix must "
+                "be under 4 GiB (T = %lld); split the token batch",
+                (long long)T);
+  return MOE_OK;
+}
+
 static moe_status run_ffn(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w, const int32_t *counts,
                           const int32_t *offsets, const int32_t *row_token, float *y_rows, float *y_sh,
                           const moe_options *o, const WsLayout &L, char *ws, hipStream_t st, hipEvent_t ev_mid) {
@@ -207,6 +222,7 @@ moe_status moe_expert_ffn(const moe_dims *dims, int64_t T, const void *u, const 
   else if (y_shared) return fail(MOE_ERR_INVALID_VALUE, "y_shared given but d_ff_shared == 0");
   WsLayout L;
   MOE_CHECK(check_ws(*dims, T, ws, ws_bytes, &L));
+  MOE_CHECK(check_path_limits(*dims, T, opts));
   hipStream_t st = (hipStream_t)stream;
   EventHook ev{opts, st};
   MOE_TRY_HIP(launch_tile_offsets(*dims, T, counts, L, (char *)ws, st), "tile offsets");
@@ -240,6 +256,7 @@ moe_status moe_layer_forward(const moe_dims *dims, int64_t T, const void *u, con
   MOE_CHECK(check_ptr(out, "out"));
   WsLayout L;
   MOE_CHECK(check_ws(*dims, T, ws, ws_bytes, &L));
+  MOE_CHECK(check_path_limits(*dims, T, opts));
   const moe_dims &dm = *dims;
   hipStream_t st = (hipStream_t)stream;
   char *w = (char *)ws;

@@ -40,7 +40,10 @@
  *
  * Limits: 1 <= top_k <= 16; 1 <= n_routed <= 1024; top_k <= n_routed;
  * d_model and d_ff (and d_ff_shared when non-zero) multiples of 64;
- * 64 <= d_model <= 32768; T * top_k < 2^31.
+ * 64 <= d_model <= 32768; T * top_k < 2^31.  On the bf16 prefill path every
+ * matrix the expert GEMMs read (u, the [T*k, f] and [T, f_s] hidden
+ * activations, each expert's weight matrix) must be under 4 GiB; larger token
+ * batches are rejected with MOE_ERR_UNSUPPORTED and must be split.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -143,3 +143,19 @@ def test_bad_options(lib):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(FileNotFoundError):
         B.Library(str(tmp_path / "libmoe.so"))
+
+
+def test_prefill_operand_limit_is_checked_before_any_launch(lib):
+    # u [T, d] of 4 GiB or more cannot be addressed by the prefill GEMMs' 32-bit
+    # offsets: rejected on the host, while the decode path has no such limit
+    d = _dims(lib, d_model=7168, n_routed=256, d_ff=2048, d_ff_shared=2048, top_k=8)
+    T = (1 << 32) // (7168 * 2) + 1
+    need = lib.workspace_size(d, T)
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.layer_forward(d, T, FAKE, _full_weights(lib), FAKE, lib.options(path=fgr.PATH_PREFILL), FAKE,
+                          ws_bytes=need, stream=0)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED and "4 GiB" in str(ei.value)
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.expert_ffn(d, T, FAKE, _full_weights(lib), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_bytes=need,
+                       stream=0)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED
