@@ -23,6 +23,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even, by
+// the hardware conversion
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// SiLU(g) = g * sigmoid(g) with the hardware exponential and reciprocal (a few
+// ulp of fp32, far below the bf16 rounding that follows)
+__device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
   union { uint4 u; bf16x8_t b; } c;
   c.u = v;

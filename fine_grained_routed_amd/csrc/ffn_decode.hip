@@ -44,7 +44,6 @@ struct DecodeArgs {
   int ns_r, ns_s;                // column slices of a routed / the shared group
 };
 
-__device__ __forceinline__ float dk_silu(float g) { return g / (1.0f + __expf(-g)); }
 
 // Weight loads are ordinary (cached) loads: each 128-byte line of a weight row
 // is requested as two 64-byte halves by two instructions, and with
@@ -163,7 +162,7 @@ __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeArgs a) {
       if (row >= valid) continue;
       if (GATEUP) {
         uint16_t *C = (uint16_t *)(shared ? a.C_sh : a.C);
-        C[(rb + row) * N + n] = f32_to_bf16(dk_silu(acc1[j][q]) * acc3[j][q]);
+        C[(rb + row) * N + n] = (uint16_t)pack_bf16x2(silu_fast(acc1[j][q]) * acc3[j][q], 0.0f);
       } else {
         float *C = (float *)(shared ? a.C_sh : a.C);
         C[(rb + row) * N + n] = acc1[j][q];

@@ -37,11 +37,13 @@
 //
 // The grid covers an upper bound of the tile count; each work-group reads the
 // device-side tile prefixes (256-row tiles), so no host sync is needed.
-// Work-groups are dispatched round-robin over the 8 XCDs, so work-group i is
-// remapped to tile (i % 8) * ceil(total / 8) + i / 8: each XCD walks a
-// contiguous range of the tile order described in the kernel, and the 32 CUs
-// of an XCD work on one expert at a time, sharing its token rows and weight
-// panels in that XCD's L2.
+// Work-groups are dispatched round-robin over the 8 XCDs.  The tile order
+// (described in the kernel) is cut into chunks of PF_CHUNK consecutive tiles,
+// dealt to the XCDs in turn: work-group i, the (i / 8)-th of XCD i % 8, takes
+// tile (((i / 8) / PF_CHUNK) * 8 + i % 8) * PF_CHUNK + (i / 8) % PF_CHUNK.  The
+// 32 CUs of an XCD work through one chunk at a time, mostly one expert,
+// sharing its token rows and weight panels in that XCD's L2, and every XCD
+// receives an even share of full and ragged tiles.
 #include <algorithm>
 
 #include "common.h"
@@ -52,6 +54,7 @@
 #define PF_BM_IDX 4  // moe_bm_of(4) == 256
 #define PF_WM 4      // 32-row sub-tiles per wave (2 x 2 waves over 8 sub-tiles)
 #define PF_GM 8      // m-tiles per ordering block (routed experts)
+#define PF_CHUNK 64  // consecutive tiles dealt to one XCD
 #define PF_GM_SH 4   // m-tiles per ordering block (shared group)
 #define PF_LOADS 8   // DMA instructions per wave per operand per k-tile (8 rows of 128 B each)
 
@@ -71,8 +74,6 @@ struct GemmArgs {
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
 // LDS rows of 64 bf16 hold eight 16-byte chunks; chunk c of row r sits in slot
 // c ^ swz(r).  swz is one-to-one on any 8 consecutive rows and on any 8 rows
@@ -315,10 +316,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
   const int mt_s = a.tile_off[a.E + 1] - mt_r;
   const int64_t tiles_r = (int64_t)mt_r * a.nt_r;
   const int64_t total = tiles_r + (int64_t)mt_s * a.nt_s;
-  const int64_t per = (total + 7) / 8;
   const int64_t slot = blockIdx.x >> 3;
-  if (slot >= per) return;
-  const int64_t tile = (int64_t)(blockIdx.x & 7) * per + slot;
+  const int64_t tile = ((slot / PF_CHUNK) * 8 + (blockIdx.x & 7)) * PF_CHUNK + slot % PF_CHUNK;
   if (tile >= total) return;
 
   bool shared;
@@ -423,10 +422,17 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
 
   // ---- epilogue.  32x32 accumulator layout (transposed product): register
   // 4q + c of lane l holds token row l % 32 of the sub-tile and output column
-  // 8q + 4 (l / 32) + c of the column tile.
+  // 8q + 4 (l / 32) + c of the column tile.  The fp32 output of the down
+  // projection goes through a private LDS slice of the wave, one 32-row
+  // sub-tile at a time (rows padded by 16 bytes), and leaves as whole 512-byte
+  // rows; the smaller bf16 output is stored directly.  First every wave's DMA
+  // has landed and every fragment read is done, so all stages are free.
+  if (!GATEUP) __syncthreads();
+  char *stg = (char *)(wv == 0 ? g_As0 : wv == 1 ? g_Bs0 : wv == 2 ? g_Bs1 : g_Bs2);
   const int mrow = lane & 31;
   const int cgrp = 4 * (lane >> 5);
   if (GATEUP) {
+    // H: each lane stores its four consecutive bf16 columns directly
     uint16_t *C = (uint16_t *)(shared ? a.C_sh : a.C);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -439,35 +445,50 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
         uint16_t *crow = C + (rb + row) * (int64_t)N + nb;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          uint32_t h[4];
+          float h[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) h[c] = f32_to_bf16(silu_f(acc[i][j][4 * q + c]) * acc[i][j + 2][4 * q + c]);
-          *(uint2 *)(crow + 8 * q) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+          for (int c = 0; c < 4; ++c) h[c] = silu_fast(acc[i][j][4 * q + c]) * acc[i][j + 2][4 * q + c];
+          *(uint2 *)(crow + 8 * q) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
         }
       }
     }
   } else {
+    // Y: 128 fp32 columns (512 bytes) per row of the wave
+    constexpr int RS = 528;
     float *C = (float *)(shared ? a.C_sh : a.C);
+    const int nb = nt * PF_BN + wn * 128;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int nb = nt * PF_BN + wn * 128 + j * 32 + cgrp;
-      if (nb >= N) continue;
+    for (int i = 0; i < PF_WM; ++i) {
+      if (i >= mw) continue;
 #pragma unroll
-      for (int i = 0; i < PF_WM; ++i) {
-        const int row = w.a0 + i * 32 + mrow;
-        if (i >= mw || row >= valid) continue;
-        float *crow = C + (rb + row) * (int64_t)N + nb;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          *(float4 *)(crow + 8 * q) = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                                  acc[i][j][4 * q + 3]);
+          *(float4 *)(stg + mrow * RS + (32 * j + 8 * q + cgrp) * 4) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      __builtin_amdgcn_wave_barrier();
+      const int col = nb + (lane & 31) * 4;  // 32 lanes per 512-byte row
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int r = (lane >> 5) + 2 * t;
+        const float4 v = *(const float4 *)(stg + r * RS + (lane & 31) * 16);
+        const int row = w.a0 + i * 32 + r;
+        if (col < N && row < valid) *(float4 *)(C + (rb + row) * (int64_t)N + col) = v;
       }
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
 
 // Upper bound of the number of 256-row m-tiles over the routed groups.
 static int64_t mtile_bound(int64_t R, int E) { return (R + PF_BM - 1) / PF_BM + std::min<int64_t>(E, R); }
+
+// Work-groups covering `tiles` under the chunked XCD deal: whole rounds of 8
+// chunks, so that every tile index below `tiles` has a work-group.
+static int64_t pf_grid(int64_t tiles) {
+  const int64_t round = 8 * PF_CHUNK;
+  return (tiles + round - 1) / round * round;
+}
 
 hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w,
                                    const int32_t *offsets, const int32_t *row_token, float *y_rows, float *y_sh,
@@ -503,8 +524,7 @@ hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u,
   g1.has_shared = hs;
   g1.nt_r = (f + PF_BN / 2 - 1) / (PF_BN / 2);
   g1.nt_s = hs ? (fs + PF_BN / 2 - 1) / (PF_BN / 2) : 1;
-  int64_t grid1 = mtile_bound(R, E) * g1.nt_r + mt_sh * g1.nt_s;
-  grid1 = ((grid1 + 7) / 8) * 8;
+  const int64_t grid1 = pf_grid(mtile_bound(R, E) * g1.nt_r + mt_sh * g1.nt_s);
   grouped_gemm_bf16_kernel<true><<<dim3((unsigned)grid1), 256, 0, st>>>(g1);
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
 
@@ -529,8 +549,7 @@ hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u,
   g2.has_shared = hs;
   g2.nt_r = (d + PF_BN - 1) / PF_BN;
   g2.nt_s = g2.nt_r;
-  int64_t grid2 = mtile_bound(R, E) * g2.nt_r + mt_sh * g2.nt_s;
-  grid2 = ((grid2 + 7) / 8) * 8;
+  const int64_t grid2 = pf_grid(mtile_bound(R, E) * g2.nt_r + mt_sh * g2.nt_s);
   grouped_gemm_bf16_kernel<false><<<dim3((unsigned)grid2), 256, 0, st>>>(g2);
   return hipGetLastError();
 }
