@@ -99,9 +99,25 @@ __host__ __device__ constexpr int moe_bm_of(int i) { return 16 << i; }  // 16 32
 // Routing block: tokens per permutation work-group.
 #define MOE_PERM_BLOCK 256
 
+// Slices of the router reduction (bf16): enough work-groups of 64 x 64
+// logits to fill the chip, each slice at least 2 k-tiles of 64 and none
+// empty: with kps = ceil(nk / S) k-tiles per slice, (S - 1) * kps < nk.
+static inline int router_splits(const moe_dims &dm, int64_t T) {
+  if (dm.dtype != MOE_BF16 || T <= 0) return 1;
+  const int64_t nk = dm.d_model / 64;
+  const int64_t tiles = ((T + 63) / 64) * ((dm.n_routed + 63) / 64);
+  const int64_t want = 256 / tiles;
+  const int64_t cap = nk / 2;
+  int64_t s = want < cap ? want : cap;
+  if (s <= 1) return 1;
+  const int64_t kps = (nk + s - 1) / s;
+  return (int)((nk + kps - 1) / kps);
+}
+
 struct WsLayout {
   size_t diag;        // DiagWords
   size_t logits;      // double [T, N_r]
+  size_t logit_part;  // double [S, T, N_r] router partial sums (S = router_splits > 1 only)
   size_t unorm2;      // double [T]   squared 2-norm of each token row
   size_t wnorm2;      // double [N_r] squared 2-norm of each router row
   size_t blk;         // int32  [nblk, N_r] per-block histograms, then bases
@@ -131,6 +147,8 @@ static inline WsLayout moe_ws_layout(const moe_dims &dm, int64_t T) {
   auto take = [&](size_t bytes) { size_t at = o; o = moe_align(o + bytes); return at; };
   L.diag = take(256);
   L.logits = take((size_t)T * E * 8);
+  const int S = router_splits(dm, T);
+  L.logit_part = take(S > 1 ? (size_t)S * T * E * 8 : 0);
   L.unorm2 = take((size_t)T * 8);
   L.wnorm2 = take(E * 8);
   L.blk = take(nblk * E * 4);

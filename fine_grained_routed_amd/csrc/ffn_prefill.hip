@@ -45,6 +45,7 @@
 // sharing its token rows and weight panels in that XCD's L2, and every XCD
 // receives an even share of full and ragged tiles.
 #include <algorithm>
+#include <utility>
 
 #include "common.h"
 
@@ -138,14 +139,26 @@ struct Operand {
 // 64w + 8q .. 64w + 8q + 7 (q < 8); lane l writes row 64w + 8q + l/8, slot
 // l%8, which holds global chunk (l%8) ^ swz(row) (folded into the offsets).
 // The k-tile's position is the scalar offset, so advancing costs one add.
+// The immediate offset applies to both the memory and the LDS address, so
+// row group q is reached as LDS base + (q % 4) KB through the immediate, with
+// the memory offset stored less that amount: a wave needs two LDS bases per
+// stage instead of eight.
+template <int Q>
+__device__ __forceinline__ void dma_group(const Operand &op, uint16_t *wstage, int koff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (lds_void_t *)(wstage + 8 * (Q & ~3) * PF_BK), 16, (int)op.off[Q],
+                                           koff, (Q & 3) * 1024, 0);
+}
+
+template <int Q0, int... Qs>
+__device__ __forceinline__ void issue_groups(const Operand &op, uint16_t *wstage, int koff,
+                                             std::integer_sequence<int, Qs...>) {
+  (dma_group<Q0 + Qs>(op, wstage, koff), ...);
+}
+
 template <int Q0 = 0, int Q1 = PF_LOADS>
 __device__ __forceinline__ void issue_op(const Operand &op, uint16_t *stage, int kt) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int koff = kt * (PF_BK * 2);
-#pragma unroll
-  for (int q = Q0; q < Q1; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(op.rsrc, (lds_void_t *)(stage + (64 * wv + 8 * q) * PF_BK), 16,
-                                             (int)op.off[q], koff, 0, 0);
+  issue_groups<Q0>(op, stage + 64 * wv * PF_BK, kt * (PF_BK * 2), std::make_integer_sequence<int, Q1 - Q0>{});
 }
 
 // Fragments of one 16-deep step: MW A row tiles and four B column tiles.
@@ -394,9 +407,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
     const int lchunk = (lane & 7) ^ swz(row);
     const int r = min(row, valid - 1);  // clamped: rows past the group are never stored
     const int64_t arow = (GATEUP && !shared) ? (int64_t)a.row_token[rb + r] : rb + r;
-    A.off[q] = (uint32_t)(arow * K * 2 + lchunk * 16);
+    // offsets are stored less the immediate offset issue_op adds (see there)
+    A.off[q] = (uint32_t)(arow * K * 2 + lchunk * 16 - (q & 3) * 1024);
     const int n = GATEUP ? nt * (PF_BN / 2) + (row & (PF_BN / 2 - 1)) : nt * PF_BN + row;
-    B.off[q] = (uint32_t)((int64_t)min(n, N - 1) * K * 2 + lchunk * 16);  // clamped: columns >= N are never stored
+    B.off[q] = (uint32_t)((int64_t)min(n, N - 1) * K * 2 + lchunk * 16 - (q & 3) * 1024);  // clamped: columns >= N are never stored
   }
 
   // LDS rows of the wave's A sub-tiles and B column tiles (gate/up: tiles 0, 1

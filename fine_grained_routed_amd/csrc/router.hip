@@ -11,7 +11,11 @@
 // fp64.  Error bound per logit (any summation order inside the chunk, unit
 // roundoff taken as 2^-22, twice truncation's 2^-23):
 //     |L - l| <= (CHUNK * 2^-22 + (d / CHUNK + 2) * 2^-52) * ||u_t|| ||c_e|| + 2^-50 |L| + d 2^-120
-// using sum |u_i c_ei| <= ||u_t|| ||c_e|| (Cauchy-Schwarz).
+// using sum |u_i c_ei| <= ||u_t|| ||c_e|| (Cauchy-Schwarz).  For small token
+// counts the reduction is split into S slices of whole chunks whose fp64
+// partial sums are added in slice order afterwards: every logit then passes
+// through at most d / CHUNK / S + S fp64 additions, never more than the
+// d / CHUNK + 2 the bound allows for.
 // fp32 inputs: products are exact in fp64 and summed in fp64:
 //     |L - l| <= (d + 2) * 2^-52 * ||u_t|| ||c_e|| + 2^-50 |L| + d 2^-120.
 #include "common.h"
@@ -57,10 +61,13 @@ __global__ __launch_bounds__(256) void row_norm2_kernel(const void *__restrict__
 // -------------------------------------------------------- bf16 logits (MFMA)
 // Work-group tile: 64 tokens x 64 experts, 4 waves in a 2 x 2 grid, each wave
 // 32 x 32 = 2 x 2 MFMA 16x16x32 tiles.
+// blockIdx.z selects a slice of kps k-tiles; with one slice the logits (bias
+// added) are written, otherwise slice s writes its fp64 partial sums to
+// logits + s * T * E and router_reduce_kernel adds them.
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const uint16_t *__restrict__ u,
                                                                  const uint16_t *__restrict__ w,
                                                                  const float *__restrict__ bias, int64_t T,
-                                                                 int E, int d, double *__restrict__ logits) {
+                                                                 int E, int d, int kps, double *__restrict__ logits) {
   __shared__ __attribute__((aligned(16))) uint16_t As[RT_BM * RT_LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[RT_BN * RT_LDS_STRIDE];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -95,14 +102,16 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const uint16_t 
     bp[q] = w + (int64_t)(bok[q] ? (e0 + lrow[q]) : 0) * d + lcol[q];
   }
   const int nk = d / RT_BK;
+  const int kt0 = blockIdx.z * kps, kt1 = min(nk, kt0 + kps);
   const int chunk_tiles = ROUTER_CHUNK / RT_BK;
-  for (int kt = 0; kt < nk; ++kt) {
-    uint4 av[2], bv[2];
+  // the next k-tile's loads are in flight while the current one is multiplied
+  uint4 av[2], bv[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      av[q] = keep_or_zero(aok[q], *(const uint4 *)(ap[q] + kt * RT_BK));  // pointers clamped in bounds
-      bv[q] = keep_or_zero(bok[q], *(const uint4 *)(bp[q] + kt * RT_BK));
-    }
+  for (int q = 0; q < 2; ++q) {
+    av[q] = keep_or_zero(aok[q], *(const uint4 *)(ap[q] + kt0 * RT_BK));  // pointers clamped in bounds
+    bv[q] = keep_or_zero(bok[q], *(const uint4 *)(bp[q] + kt0 * RT_BK));
+  }
+  for (int kt = kt0; kt < kt1; ++kt) {
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -110,6 +119,12 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const uint16_t 
       *(uint4 *)&Bs[lrow[q] * RT_LDS_STRIDE + lcol[q]] = bv[q];
     }
     __syncthreads();
+    const int kn = min(kt + 1, kt1 - 1);  // the last trip re-loads its own tile (in bounds, unused)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      av[q] = keep_or_zero(aok[q], *(const uint4 *)(ap[q] + kn * RT_BK));
+      bv[q] = keep_or_zero(bok[q], *(const uint4 *)(bp[q] + kn * RT_BK));
+    }
 #pragma unroll
     for (int kk = 0; kk < RT_BK / 32; ++kk) {
       bf16x8_t a[2], b[2];
@@ -126,7 +141,7 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const uint16_t 
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if ((kt + 1) % chunk_tiles == 0 || kt + 1 == nk) {
+    if ((kt + 1) % chunk_tiles == 0 || kt + 1 == kt1) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -144,13 +159,26 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const uint16_t 
     for (int j = 0; j < 2; ++j) {
       const int e = e0 + wn * 32 + j * 16 + (lane & 15);
       if (e >= E) continue;
-      const double b = bias ? (double)bias[e] : 0.0;
+      const bool whole = gridDim.z == 1;
+      const double b = (whole && bias) ? (double)bias[e] : 0.0;
+      double *dst = logits + (whole ? 0 : (int64_t)blockIdx.z * T * E);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t t = t0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
-        if (t < T) logits[t * E + e] = acc64[i][j][r] + b;
+        if (t < T) dst[t * E + e] = acc64[i][j][r] + b;
       }
     }
+}
+
+// logits[t, e] = sum over slices s = 0, 1, ... of part[s][t][e] (in this
+// order) + b_e.
+__global__ __launch_bounds__(256) void router_reduce_kernel(const double *__restrict__ part, int S, int64_t n, int E,
+                                                            const float *__restrict__ bias, double *__restrict__ logits) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  double s = part[i];
+  for (int k = 1; k < S; ++k) s += part[(int64_t)k * n + i];
+  logits[i] = s + (bias ? (double)bias[i % E] : 0.0);
 }
 
 // ------------------------------------------------------ fp32 logits (fp64 VALU)
@@ -190,9 +218,17 @@ hipError_t launch_router_logits(const moe_dims &dm, int64_t T, const void *u, co
   if (dm.dtype == MOE_BF16) {
     row_norm2_kernel<true><<<dim3((unsigned)((T + 3) / 4)), 256, 0, st>>>(u, T, d, un2);
     row_norm2_kernel<true><<<dim3((unsigned)((E + 3) / 4)), 256, 0, st>>>(w_router, E, d, wn2);
-    dim3 grid((unsigned)((T + RT_BM - 1) / RT_BM), (unsigned)((E + RT_BN - 1) / RT_BN));
+    const int nk = d / RT_BK;
+    const int S = router_splits(dm, T);
+    const int kps = (nk + S - 1) / S;
+    dim3 grid((unsigned)((T + RT_BM - 1) / RT_BM), (unsigned)((E + RT_BN - 1) / RT_BN), (unsigned)S);
+    double *part = S > 1 ? (double *)(ws + L.logit_part) : logits;
     router_logits_bf16_kernel<<<grid, 256, 0, st>>>((const uint16_t *)u, (const uint16_t *)w_router, bias, T, E, d,
-                                                    logits);
+                                                    kps, part);
+    if (S > 1) {
+      const int64_t n = T * E;
+      router_reduce_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(part, S, n, E, bias, logits);
+    }
   } else {
     row_norm2_kernel<false><<<dim3((unsigned)((T + 3) / 4)), 256, 0, st>>>(u, T, d, un2);
     row_norm2_kernel<false><<<dim3((unsigned)((E + 3) / 4)), 256, 0, st>>>(w_router, E, d, wn2);
