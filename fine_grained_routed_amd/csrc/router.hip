@@ -176,8 +176,16 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const double *__rest
                                                             const float *__restrict__ bias, double *__restrict__ logits) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  double s = part[i];
-  for (int k = 1; k < S; ++k) s += part[(int64_t)k * n + i];
+  // loads in batches of 8 (in flight together), additions in slice order
+  double s = 0.0;
+  for (int k0 = 0; k0 < S; k0 += 8) {
+    double v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = k0 + q < S ? part[(int64_t)(k0 + q) * n + i] : 0.0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (k0 + q < S) s = (k0 + q == 0) ? v[q] : s + v[q];
+  }
   logits[i] = s + (bias ? (double)bias[i % E] : 0.0);
 }
 
