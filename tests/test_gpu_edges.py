@@ -148,3 +148,14 @@ def test_decode_matches_prefill_prefix(lib):
     ud = workloads.make_u(dec, device="cuda")
     up = workloads.make_u(pre, device="cuda")
     assert torch.equal(ud, up[:64])
+
+
+@pytest.mark.parametrize("path", [PATH_PREFILL, PATH_DECODE])
+@pytest.mark.parametrize("T,d,E,f,k", [
+    (100, 32768, 16, 64, 4),   # widest model dimension the interface accepts
+    (300, 64, 1024, 64, 16),   # most experts and the largest top-k, narrowest model dimension
+], ids=["d32768", "E1024_k16"])
+def test_interface_limits(lib, path, T, d, E, f, k):
+    wl = _wl(T, d, E, f, 1, k, name=f"limits_{d}_{E}")
+    inp = gpu_inputs(wl, seed=9)
+    check_case(_layer(inp, wl), inp, wl, path=path)
