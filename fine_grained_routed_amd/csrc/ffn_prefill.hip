@@ -370,17 +370,22 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
     nt = in_blk / bsize;
     mt = (int)blk * gm + in_blk % bsize;
   }
-  if (!shared) {
-    const int m0 = mt * PF_BM;
-    valid = min(PF_BM, a.offsets[g + 1] - a.offsets[g] - m0);
-    rb = (int64_t)a.offsets[g] + m0;
-  } else {
-    rb = (int64_t)mt * PF_BM;
-    valid = (int)min((int64_t)PF_BM, a.T - rb);
+  // the group's rows are cut into its mt_g tiles as evenly as possible (all
+  // of them at most 256 rows), so a group slightly over a multiple of 256 rows
+  // gets tiles of nearly equal size rather than a nearly empty last tile
+  {
+    const int64_t rows = shared ? a.T : (int64_t)(a.offsets[g + 1] - a.offsets[g]);
+    const int64_t r0 = (int64_t)mt * rows / mt_g, r1 = (int64_t)(mt + 1) * rows / mt_g;
+    valid = (int)(r1 - r0);
+    rb = (shared ? 0 : (int64_t)a.offsets[g]) + r0;
   }
   const int wm = wv >> 1, wn = wv & 1;  // 2 x 2 wave layout
-  // 32-row sub-tiles of this wave's 128 rows that hold rows of the group
-  const int mw = min(PF_WM, max(0, ((valid + 31) >> 5) - PF_WM * wm));
+  // the tile's 32-row sub-tiles, split as evenly as possible between the two
+  // wave rows (the first takes the odd one): mw of them from row a0 on
+  const int ns = (valid + 31) >> 5;
+  const int mw0 = (ns + 1) >> 1;
+  const int mw = wm == 0 ? mw0 : ns - mw0;
+  const int a0 = wm == 0 ? 0 : 32 * mw0;
 
   // ---- DMA sources: lane l of wave w fetches, for q < 8, row 64w + 8q + l/8,
   // chunk (l%8) ^ swz(row) = (l%8) ^ ((l/8) ^ q) of each operand.  Byte
@@ -416,7 +421,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
   // LDS rows of the wave's A sub-tiles and B column tiles (gate/up: tiles 0, 1
   // are gate columns, 2, 3 the same columns of up)
   WaveRows w;
-  w.a0 = wm * (PF_BM / 2);
+  w.a0 = a0;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     w.b[j] = GATEUP ? (j >> 1) * (PF_BN / 2) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
