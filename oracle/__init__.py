@@ -18,6 +18,14 @@ from .moe_oracle import (  # noqa: F401
     combine,
     forward,
     forward_dense,
+    capacity_seats,
+)
+from .block import (  # noqa: F401
+    round_to_bf16,
+    store,
+    rms_norm,
+    dense_ffn,
+    block_forward,
 )
 from .accounting import (  # noqa: F401
     combinations,

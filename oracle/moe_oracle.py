@@ -29,7 +29,9 @@ the design notes):
   stored inputs; exact ties go to the lower expert index; the k slots are in
   descending key order;
 * the shared output is added with coefficient 1 and no residual is added;
-* every token goes to all of its k experts (no capacity limit).
+* every token goes to all of its k experts unless a capacity (seats per
+  expert) is given; then each expert keeps the first seats of its pairs in
+  token order and the dropped slots contribute nothing.
 
 Inputs are numpy arrays holding the exact stored values (fp32 or bf16 widened
 to fp64, which is exact).  Expert weight stacks may be any object whose
@@ -152,26 +154,52 @@ def route(u, w_router, k: int, bias=None):
 
 
 # ---------------------------------------------------------------------- permutation
-def permute(topk_idx, n_routed: int):
+def permute(topk_idx, n_routed: int, capacity: Optional[int] = None):
     """Group the T*k (token, slot) pairs by expert, tokens ascending inside a group.
 
-    Returns counts [N_r], offsets [N_r+1] (exclusive prefix, offsets[N_r] =
-    T*k), row_token [T*k] (row r of expert group -> its token) and token_row
-    [T,k] (token t's slot j -> its row).  This is the expert-to-token grouping
-    that feeds the scatter-sum of routed expert outputs ("Shared Expert", How it
-    works).
+    Returns counts [N_r], offsets [N_r+1] (exclusive prefix of counts),
+    row_token [offsets[N_r]] (row r of an expert group -> its token) and
+    token_row [T,k] (token t's slot j -> its row, or -1 when the pair was
+    dropped).  This is the expert-to-token grouping that feeds the scatter-sum
+    of routed expert outputs ("Shared Expert", How it works).
+
+    capacity: seats per expert ("What is an 'expert', really?", glossary:
+    capacity factor / token dropping -- each expert takes at most a fixed
+    number of tokens per batch and the overflow is skipped).  Reading: an
+    expert keeps the first ``capacity`` of its pairs in token order, i.e. a
+    prefix of its group in the stable grouping; the rest are dropped and
+    contribute nothing.  None = no limit (every pair kept).
     """
     idx = np.asarray(topk_idx, dtype=np.int64)
     T, k = idx.shape
     flat = idx.ravel()
-    counts = np.bincount(flat, minlength=n_routed).astype(np.int32)
+    raw = np.bincount(flat, minlength=n_routed)
+    order = np.argsort(flat, kind="stable")  # pairs grouped by expert, token order inside
+    start = np.zeros(n_routed + 1, dtype=np.int64)
+    np.cumsum(raw, out=start[1:])
+    rank = np.empty(T * k, dtype=np.int64)  # position of each pair inside its expert's group
+    rank[order] = np.arange(T * k) - start[flat[order]]
+    seats = raw if capacity is None else np.minimum(raw, capacity)
+    keep = np.ones(T * k, dtype=bool) if capacity is None else rank < capacity
     offsets = np.zeros(n_routed + 1, dtype=np.int64)
-    np.cumsum(counts, out=offsets[1:])
-    order = np.argsort(flat, kind="stable")
-    row_token = (order // k).astype(np.int32)
-    token_row = np.empty(T * k, dtype=np.int64)
-    token_row[order] = np.arange(T * k)
-    return counts, offsets.astype(np.int32), row_token, token_row.reshape(T, k).astype(np.int32)
+    np.cumsum(seats, out=offsets[1:])
+    token_row = np.full(T * k, -1, dtype=np.int64)
+    token_row[keep] = offsets[flat[keep]] + rank[keep]
+    row_token = np.empty(int(offsets[-1]), dtype=np.int64)
+    row_token[token_row[keep]] = np.nonzero(keep)[0] // k
+    return (seats.astype(np.int32), offsets.astype(np.int32), row_token.astype(np.int32),
+            token_row.reshape(T, k).astype(np.int32))
+
+
+def capacity_seats(capacity_factor, T: int, k: int, n_routed: int) -> int:
+    """Seats per expert for a capacity factor: ceil(cf * T * k / N_r), exactly.
+
+    The glossary of "What is an 'expert', really?" gives each expert a seat
+    limit per batch; the usual way to size it from a capacity factor is cf
+    times the balanced load T*k/N_r, rounded up.  cf is taken as the exact
+    rational value of the given number (a float is its binary value)."""
+    q = Fraction(capacity_factor) * T * k / n_routed
+    return int(-((-q.numerator) // q.denominator))
 
 
 # -------------------------------------------------------------------------- experts
@@ -217,21 +245,27 @@ def combine(y_rows, y_shared, topk_w, token_row):
 
     The shared term enters with coefficient exactly 1, is not scaled by any
     gate nor by 1/N_s ("Shared Expert", Overview and Watch-outs), and no
-    residual is added (MoE.forward returns shared + routed only)."""
+    residual is added (MoE.forward returns shared + routed only).  A slot whose
+    pair was dropped for capacity (token_row -1) contributes nothing."""
     y_rows = _f64(y_rows)
     g = _f64(topk_w)
     T, k = g.shape
-    out = np.zeros((T, y_rows.shape[1]), dtype=np.float64) if y_shared is None else _f64(y_shared).copy()
+    d = y_rows.shape[1] if y_shared is None else np.shape(y_shared)[1]
+    out = np.zeros((T, d), dtype=np.float64) if y_shared is None else _f64(y_shared).copy()
+    tr = np.asarray(token_row)
     for j in range(k):
-        out += g[:, j, None] * y_rows[np.asarray(token_row)[:, j]]
+        kept = tr[:, j] >= 0
+        out[kept] += g[kept, j, None] * y_rows[tr[kept, j]]
     return out
 
 
-def forward(u, w_router, w1, w3, w2, k: int, bias=None, w1s=None, w3s=None, w2s=None):
-    """The whole layer: route, group, run experts, combine.  Returns a dict."""
+def forward(u, w_router, w1, w3, w2, k: int, bias=None, w1s=None, w3s=None, w2s=None,
+            capacity: Optional[int] = None):
+    """The whole layer: route, group, run experts, combine.  Returns a dict.
+    capacity: seats per expert (see ``permute``); None = no limit."""
     E = _f64(w_router).shape[0]
     idx, gates, l, n_exact = route(u, w_router, k, bias)
-    counts, offsets, row_token, token_row = permute(idx, E)
+    counts, offsets, row_token, token_row = permute(idx, E, capacity)
     y_rows, y_shared = expert_ffn(u, w1, w3, w2, counts, offsets, row_token, w1s, w3s, w2s)
     out = combine(y_rows, y_shared, gates, token_row)
     routed = combine(y_rows, None, gates, token_row)

@@ -15,6 +15,13 @@ Recipe (the shapes come from the pages; the distributions are the workload's):
   normalisation belongs to the input recipe, not to the layer.
 * every weight: 0.02 * N(0, 1) computed in fp32 (0.02 is the standard
   deviation), then rounded to bf16 (RNE) for the bf16 workloads.
+* block inputs (the pre-norm residual stream, for the block entry point):
+  x[t, :] = s_t * z_t with z_t ~ N(0, 1) and a per-token scale
+  s_t = 2^N(0, 1) (so token norms spread over about a factor 4 either way),
+  computed in fp32 and rounded to the workload dtype; the RMSNorm gain
+  gamma = 1 + 0.1 * N(0, 1) in fp32; eps = NORM_EPS.
+* dense workloads (no routed experts, top-k 0): the dense prefix FFN, whose
+  weights are the "shared" triple w1s, w3s, w2s of width d_ff.
 * skewed workloads: a per-expert router bias b_e = -1.2 * ln(e + 1) (a Zipf
   s = 1.2 profile over expert rank e + 1), rounded to fp32.  It is added to the
   router logits before the softmax.
@@ -45,9 +52,12 @@ __all__ = [
     "sample_tokens",
     "ROW_BLOCK",
     "F64Experts",
+    "make_block_inputs",
+    "NORM_EPS",
 ]
 
 ROW_BLOCK = 64  # rows of u drawn per generator
+NORM_EPS = 1e-6  # RMSNorm epsilon of the block workloads
 
 
 @dataclasses.dataclass(frozen=True)
@@ -105,10 +115,19 @@ WORKLOADS: Dict[str, Workload] = {
                  "512 routed f=512 + 1 shared, top-10, Zipf(1.2) router bias"),
         Workload("skew128_top1", 8192, 2048, 128, 512, 1, 1, "bf16", "zipf1.2", "skew128",
                  "128 routed f=512 + 1 shared, top-1, Zipf(1.2) router bias"),
+        Workload("dense_small", 1000, 256, 0, 640, 1, 0, "bf16", None, "dsmall",
+                 "dense SwiGLU FFN (no routed experts): d=256, width 640"),
+        Workload("dense_small_f32", 300, 128, 0, 192, 1, 0, "f32", None, "dsmallf",
+                 "dense SwiGLU FFN (no routed experts): d=128, width 192, fp32"),
+        Workload("dsv3_dense_prefill", 16384, 7168, 0, 18432, 1, 0, "bf16", None, "dsv3dense",
+                 "DeepSeek-V3 dense prefix layer FFN: d=7168, width 18432, T=16384"),
+        Workload("dsv3_dense_decode", 64, 7168, 0, 18432, 1, 0, "bf16", None, "dsv3dense",
+                 "DeepSeek-V3 dense prefix layer FFN: same weights, T=64"),
     ]
 }
 
-TENSOR_IDS = {"u": 0, "w_router": 1, "w1": 2, "w3": 3, "w2": 4, "w1s": 5, "w3s": 6, "w2s": 7}
+TENSOR_IDS = {"u": 0, "w_router": 1, "w1": 2, "w3": 3, "w2": 4, "w1s": 5, "w3s": 6, "w2s": 7, "x": 8, "gamma": 9,
+              "xscale": 10}
 
 
 def get(name: str) -> Workload:
@@ -177,6 +196,27 @@ def make_inputs(wl: Workload, seed: int = 0, device="cpu", T: Optional[int] = No
     """All inputs of one layer forward: dict with ``u`` plus the weights."""
     inp = make_weights(wl, seed, device)
     inp["u"] = make_u(wl, seed, device, T)
+    return inp
+
+
+def make_x(wl: Workload, seed: int = 0, device="cpu", T: Optional[int] = None) -> torch.Tensor:
+    """Raw residual stream [T, d] (before the pre-norm), in the workload dtype."""
+    T = wl.T if T is None else T
+    out = torch.empty((T, wl.d), dtype=_tdtype(wl.dtype), device=device)
+    for b in range((T + ROW_BLOCK - 1) // ROW_BLOCK):
+        z = _randn((ROW_BLOCK, wl.d), _seed(seed, wl.family, "x", b), device)
+        s = torch.exp2(_randn((ROW_BLOCK, 1), _seed(seed, wl.family, "xscale", b), device))
+        rows = min(ROW_BLOCK, T - b * ROW_BLOCK)
+        out[b * ROW_BLOCK: b * ROW_BLOCK + rows] = (z * s)[:rows].to(out.dtype)
+    return out
+
+
+def make_block_inputs(wl: Workload, seed: int = 0, device="cpu", T: Optional[int] = None):
+    """Inputs of one pre-norm block: the weights, the raw stream ``x`` and the
+    RMSNorm gain ``gamma`` [d] fp32 (no ``u``: the block computes it)."""
+    inp = make_weights(wl, seed, device)
+    inp["x"] = make_x(wl, seed, device, T)
+    inp["gamma"] = 1.0 + 0.1 * _randn((wl.d,), _seed(seed, wl.family, "gamma", 0), device)
     return inp
 
 
