@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     MoeError,
     Options,
     Weights,
+    capacity_seats,
     load,
 )
 from .layer import MoELayer  # noqa: F401

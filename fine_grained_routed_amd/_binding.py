@@ -21,7 +21,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_VALUE", 2: "MOE_ERR_UNSUPPORTED
 
 # the functions include/moe.h declares
 EXPORTS = ("moe_workspace_size", "moe_router_topk", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_layer_forward", "moe_read_diagnostics", "moe_last_error")
+           "moe_layer_forward", "moe_rmsnorm", "moe_block_forward", "moe_read_diagnostics", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -33,7 +33,7 @@ class MoeError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_routed", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("d_ff_shared", ctypes.c_int32), ("top_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -65,6 +65,9 @@ _SIG = {
     "moe_combine": [ctypes.POINTER(Dims), _I64, _P, _P, _P, _P, _P, _P],
     "moe_layer_forward": [ctypes.POINTER(Dims), _I64, _P, ctypes.POINTER(Weights), _P, ctypes.POINTER(Options), _P,
                           ctypes.c_size_t, _P],
+    "moe_rmsnorm": [ctypes.POINTER(Dims), _I64, _P, _P, ctypes.c_double, _P, _P],
+    "moe_block_forward": [ctypes.POINTER(Dims), _I64, _P, _P, ctypes.c_double, ctypes.POINTER(Weights), _P,
+                          ctypes.POINTER(Options), _P, ctypes.c_size_t, _P],
     "moe_read_diagnostics": [_P, ctypes.POINTER(Diag), _P],
 }
 
@@ -109,8 +112,8 @@ class Library:
             raise MoeError(status, self.last_error())
 
     @staticmethod
-    def dims(d_model, n_routed, d_ff, d_ff_shared, top_k, dtype=MOE_BF16, out_dtype=MOE_F32) -> Dims:
-        return Dims(d_model, n_routed, d_ff, d_ff_shared, top_k, dtype, out_dtype)
+    def dims(d_model, n_routed, d_ff, d_ff_shared, top_k, dtype=MOE_BF16, out_dtype=MOE_F32, capacity=0) -> Dims:
+        return Dims(d_model, n_routed, d_ff, d_ff_shared, top_k, dtype, out_dtype, capacity)
 
     @staticmethod
     def weights(w_router=None, router_bias=None, w1=None, w3=None, w2=None, w1s=None, w3s=None, w2s=None) -> Weights:
@@ -163,10 +166,30 @@ class Library:
                                                ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes,
                                                _stream(stream)))
 
+    def rmsnorm(self, dims, T, x, norm_weight, eps, u, stream=None):
+        self._check(self.lib.moe_rmsnorm(ctypes.byref(dims), T, _ptr(x), _ptr(norm_weight), float(eps), _ptr(u),
+                                         _stream(stream)))
+
+    def block_forward(self, dims, T, x, norm_weight, eps, weights: Weights, out, options: Optional[Options], ws,
+                      ws_bytes=None, stream=None):
+        self._check(self.lib.moe_block_forward(ctypes.byref(dims), T, _ptr(x), _ptr(norm_weight), float(eps),
+                                               ctypes.byref(weights), _ptr(out),
+                                               None if options is None else ctypes.byref(options), _ptr(ws),
+                                               ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes,
+                                               _stream(stream)))
+
     def read_diagnostics(self, ws, stream=None) -> dict:
         d = Diag()
         self._check(self.lib.moe_read_diagnostics(_ptr(ws), ctypes.byref(d), _stream(stream)))
         return d.as_dict()
+
+
+def capacity_seats(capacity_factor, T: int, top_k: int, n_routed: int) -> int:
+    """Seats per expert for a capacity factor: ceil(cf * T * top_k / n_routed), in
+    exact rational arithmetic on the value of cf (a float counts as its binary value)."""
+    from fractions import Fraction
+    q = Fraction(capacity_factor) * T * top_k / n_routed
+    return -((-q.numerator) // q.denominator)
 
 
 _LOADED: Optional[Library] = None

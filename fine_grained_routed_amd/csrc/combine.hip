@@ -1,25 +1,30 @@
 // Combine: out[t,:] = y_shared[t,:] + sum_{j<k} w[t,j] * y_rows[token_row[t,j], :]
-// accumulated in fp32 in slot order (start from 0 when there is no shared term).
+// accumulated in fp32 in slot order (start from 0 when there is no shared term),
+// then, for the pre-norm block, plus the raw block input x[t,:].
 //
 // Source: "Shared Expert" (How it works: the shared output is added to the
-// scatter-sum of routed expert outputs; Overview and Watch-outs: coefficient
-// exactly 1, no gate and no 1/N_s; Official code: no residual inside the
-// layer).  The scatter-sum is done as a gather per token so that the order of
-// the additions is fixed and the result deterministic.
+// scatter-sum of routed expert outputs, and eq. 12's residual is added at
+// block level; Overview and Watch-outs: coefficient exactly 1, no gate and no
+// 1/N_s; Official code: no residual inside MoE.forward).  The scatter-sum is
+// done as a gather per token so that the order of the additions is fixed and
+// the result deterministic.  Slots dropped for capacity (token_row -1) add
+// nothing.
 #include "common.h"
 
 #define CB_MAXK 16
 
-// KM: top_k rounded up to 1, 2, 4, 8 or 16 (slots j >= k are predicated off)
-template <bool OUT_BF16, int KM>
+// KM: top_k rounded up to 0, 1, 2, 4, 8 or 16 (slots j >= k are predicated off;
+// 0 = dense layer, shared term only).  RES: 0 no residual, 1 fp32, 2 bf16 x.
+template <bool OUT_BF16, int KM, int RES>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y_rows, const float *__restrict__ y_sh,
                                                       const float *__restrict__ topk_w,
-                                                      const int32_t *__restrict__ token_row, int64_t T, int d, int k,
+                                                      const int32_t *__restrict__ token_row,
+                                                      const void *__restrict__ resid, int64_t T, int d, int k,
                                                       void *__restrict__ out) {
   const int64_t t = blockIdx.x;
   __shared__ int64_t rows[CB_MAXK];
   __shared__ float gw[CB_MAXK];
-  if (threadIdx.x < CB_MAXK) {
+  if (KM > 0 && threadIdx.x < CB_MAXK) {
     const bool slot = (int)threadIdx.x < k;
     rows[threadIdx.x] = slot ? (int64_t)token_row[t * k + threadIdx.x] : -1;
     gw[threadIdx.x] = slot ? topk_w[t * k + threadIdx.x] : 0.f;
@@ -29,11 +34,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   for (int c = threadIdx.x * 4; c < d; c += 256 * 4) {
     // every row of the token is loaded before the first addition, so the k
     // loads are in flight together; the additions then run in slot order
-    float4 y[KM];
+    float4 y[KM > 0 ? KM : 1];
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
-      const int64_t r = rows[j];        // -1 past the token's k slots
-      const bool ok = r >= 0 && r < R;  // an invalid caller row contributes nothing
+      const int64_t r = rows[j];        // -1 past the token's k slots or for a dropped pair
+      const bool ok = r >= 0 && r < R;  // an invalid row contributes nothing
       const float4 v = *(const float4 *)(y_rows + (ok ? r : 0) * d + c);
       y[j] = make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
     }
@@ -48,6 +53,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
         acc.w = fmaf(g, y[j].w, acc.w);
       }
     }
+    if (RES == 1) {
+      const float4 x = *(const float4 *)((const float *)resid + t * d + c);
+      acc = make_float4(x.x + acc.x, x.y + acc.y, x.z + acc.z, x.w + acc.w);
+    } else if (RES == 2) {
+      const uint2 xb = *(const uint2 *)((const uint16_t *)resid + t * d + c);
+      acc.x = bf16_to_f32((uint16_t)xb.x) + acc.x;
+      acc.y = bf16_to_f32((uint16_t)(xb.x >> 16)) + acc.y;
+      acc.z = bf16_to_f32((uint16_t)xb.y) + acc.z;
+      acc.w = bf16_to_f32((uint16_t)(xb.y >> 16)) + acc.w;
+    }
     if (OUT_BF16) {
       uint16_t *o = (uint16_t *)out + t * d + c;
       uint2 pk;
@@ -60,29 +75,43 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   }
 }
 
-template <bool OUT_BF16, int KM>
-static void launch_combine_k(const moe_dims &dm, int64_t T, const float *y_rows, const float *y_sh,
-                             const float *topk_w, const int32_t *token_row, void *out, hipStream_t st) {
-  combine_kernel<OUT_BF16, KM><<<dim3((unsigned)T), 256, 0, st>>>(y_rows, y_sh, topk_w, token_row, T, dm.d_model,
-                                                                  dm.top_k, out);
+struct CombineCall {
+  const float *y_rows, *y_sh, *topk_w;
+  const int32_t *token_row;
+  const void *resid;
+  void *out;
+};
+
+template <bool OUT_BF16, int KM, int RES>
+static void launch_combine_k(const moe_dims &dm, int64_t T, const CombineCall &c, hipStream_t st) {
+  combine_kernel<OUT_BF16, KM, RES><<<dim3((unsigned)T), 256, 0, st>>>(c.y_rows, c.y_sh, c.topk_w, c.token_row,
+                                                                       c.resid, T, dm.d_model, dm.top_k, c.out);
+}
+
+template <bool OUT_BF16, int RES>
+static void launch_combine_r(const moe_dims &dm, int64_t T, const CombineCall &c, hipStream_t st) {
+  const int k = dm.top_k;
+  if (k <= 0) launch_combine_k<OUT_BF16, 0, RES>(dm, T, c, st);
+  else if (k <= 1) launch_combine_k<OUT_BF16, 1, RES>(dm, T, c, st);
+  else if (k <= 2) launch_combine_k<OUT_BF16, 2, RES>(dm, T, c, st);
+  else if (k <= 4) launch_combine_k<OUT_BF16, 4, RES>(dm, T, c, st);
+  else if (k <= 8) launch_combine_k<OUT_BF16, 8, RES>(dm, T, c, st);
+  else launch_combine_k<OUT_BF16, CB_MAXK, RES>(dm, T, c, st);
 }
 
 template <bool OUT_BF16>
-static void launch_combine_t(const moe_dims &dm, int64_t T, const float *y_rows, const float *y_sh,
-                             const float *topk_w, const int32_t *token_row, void *out, hipStream_t st) {
-  const int k = dm.top_k;
-  if (k <= 1) launch_combine_k<OUT_BF16, 1>(dm, T, y_rows, y_sh, topk_w, token_row, out, st);
-  else if (k <= 2) launch_combine_k<OUT_BF16, 2>(dm, T, y_rows, y_sh, topk_w, token_row, out, st);
-  else if (k <= 4) launch_combine_k<OUT_BF16, 4>(dm, T, y_rows, y_sh, topk_w, token_row, out, st);
-  else if (k <= 8) launch_combine_k<OUT_BF16, 8>(dm, T, y_rows, y_sh, topk_w, token_row, out, st);
-  else launch_combine_k<OUT_BF16, CB_MAXK>(dm, T, y_rows, y_sh, topk_w, token_row, out, st);
+static void launch_combine_t(const moe_dims &dm, int64_t T, const CombineCall &c, hipStream_t st) {
+  if (!c.resid) launch_combine_r<OUT_BF16, 0>(dm, T, c, st);
+  else if (dm.dtype == MOE_BF16) launch_combine_r<OUT_BF16, 2>(dm, T, c, st);
+  else launch_combine_r<OUT_BF16, 1>(dm, T, c, st);
 }
 
 hipError_t launch_combine(const moe_dims &dm, int64_t T, const float *y_rows, const float *y_sh, const float *topk_w,
-                          const int32_t *token_row, void *out, hipStream_t st) {
+                          const int32_t *token_row, const void *resid, void *out, hipStream_t st) {
+  const CombineCall c{y_rows, y_sh, topk_w, token_row, resid, out};
   if (dm.out_dtype == MOE_BF16)
-    launch_combine_t<true>(dm, T, y_rows, y_sh, topk_w, token_row, out, st);
+    launch_combine_t<true>(dm, T, c, st);
   else
-    launch_combine_t<false>(dm, T, y_rows, y_sh, topk_w, token_row, out, st);
+    launch_combine_t<false>(dm, T, c, st);
   return hipGetLastError();
 }

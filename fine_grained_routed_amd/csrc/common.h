@@ -103,7 +103,7 @@ __host__ __device__ constexpr int moe_bm_of(int i) { return 16 << i; }  // 16 32
 // logits to fill the chip, each slice at least 2 k-tiles of 64 and none
 // empty: with kps = ceil(nk / S) k-tiles per slice, (S - 1) * kps < nk.
 static inline int router_splits(const moe_dims &dm, int64_t T) {
-  if (dm.dtype != MOE_BF16 || T <= 0) return 1;
+  if (dm.dtype != MOE_BF16 || T <= 0 || dm.n_routed <= 0) return 1;
   const int64_t nk = dm.d_model / 64;
   const int64_t tiles = ((T + 63) / 64) * ((dm.n_routed + 63) / 64);
   const int64_t want = 256 / tiles;
@@ -132,6 +132,7 @@ struct WsLayout {
   size_t token_row;   // int32 [T, k]
   size_t y_rows;      // f32 [R, d]
   size_t y_sh;        // f32 [T, d]
+  size_t u_norm;      // dtype [T, d] RMS-normalised input (block forward only)
   size_t total;
 };
 
@@ -163,6 +164,7 @@ static inline WsLayout moe_ws_layout(const moe_dims &dm, int64_t T) {
   L.token_row = take(R * 4);
   L.y_rows = take(R * d * 4);
   L.y_sh = take((size_t)T * d * 4);
+  L.u_norm = take((size_t)T * d * hbytes);
   L.total = o;
   return L;
 }
@@ -187,5 +189,9 @@ hipError_t launch_ffn_decode(const moe_dims &dm, int64_t T, const void *u, const
                              const int32_t *counts, const int32_t *offsets, const int32_t *row_token,
                              float *y_rows, float *y_sh, const WsLayout &L, char *ws, hipStream_t st,
                              hipEvent_t ev_mid);
+// resid: NULL, or the block's raw input x [T, d] in dm.dtype, added last
 hipError_t launch_combine(const moe_dims &dm, int64_t T, const float *y_rows, const float *y_sh,
-                          const float *topk_w, const int32_t *token_row, void *out, hipStream_t st);
+                          const float *topk_w, const int32_t *token_row, const void *resid, void *out,
+                          hipStream_t st);
+hipError_t launch_rmsnorm(const moe_dims &dm, int64_t T, const void *x, const float *gamma, double eps, void *u,
+                          hipStream_t st);

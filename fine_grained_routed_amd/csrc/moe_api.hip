@@ -40,11 +40,18 @@ static bool al16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 static moe_status check_dims(const moe_dims *dm, int64_t T) {
   if (!dm) return fail(MOE_ERR_INVALID_VALUE, "dims is NULL");
   if (T < 0) return fail(MOE_ERR_INVALID_VALUE, "T < 0");
-  if (dm->top_k < 1) return fail(MOE_ERR_INVALID_VALUE, "top_k < 1");
-  if (dm->n_routed < 1) return fail(MOE_ERR_INVALID_VALUE, "n_routed < 1");
-  if (dm->top_k > dm->n_routed) return fail(MOE_ERR_INVALID_VALUE, "top_k > n_routed");
-  if (dm->d_model < 1 || dm->d_ff < 1 || dm->d_ff_shared < 0)
-    return fail(MOE_ERR_INVALID_VALUE, "non-positive width");
+  const bool dense = dm->n_routed == 0;
+  if (dense) {
+    if (dm->top_k != 0) return fail(MOE_ERR_INVALID_VALUE, "a dense layer (n_routed == 0) needs top_k == 0");
+    if (dm->d_ff_shared < 1) return fail(MOE_ERR_INVALID_VALUE, "a dense layer (n_routed == 0) needs d_ff_shared > 0");
+  } else {
+    if (dm->top_k < 1) return fail(MOE_ERR_INVALID_VALUE, "top_k < 1");
+    if (dm->n_routed < 1) return fail(MOE_ERR_INVALID_VALUE, "n_routed < 0");
+    if (dm->top_k > dm->n_routed) return fail(MOE_ERR_INVALID_VALUE, "top_k > n_routed");
+    if (dm->d_ff < 1) return fail(MOE_ERR_INVALID_VALUE, "non-positive width");
+  }
+  if (dm->d_model < 1 || dm->d_ff < 0 || dm->d_ff_shared < 0) return fail(MOE_ERR_INVALID_VALUE, "non-positive width");
+  if (dm->capacity < 0) return fail(MOE_ERR_INVALID_VALUE, "capacity < 0");
   if (dm->dtype != MOE_F32 && dm->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dm->dtype);
   if (dm->out_dtype != MOE_F32 && dm->out_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "unknown out_dtype %d", dm->out_dtype);
@@ -56,6 +63,11 @@ static moe_status check_dims(const moe_dims *dm, int64_t T) {
   if (dm->d_ff_shared % 64 || dm->d_ff_shared > 65536)
     return fail(MOE_ERR_UNSUPPORTED, "d_ff_shared must be a multiple of 64, <= 65536");
   if (T * (int64_t)dm->top_k >= (int64_t)1 << 31) return fail(MOE_ERR_UNSUPPORTED, "T * top_k >= 2^31");
+  return MOE_OK;
+}
+
+static moe_status need_routed(const moe_dims &dm) {
+  if (dm.n_routed < 1) return fail(MOE_ERR_INVALID_VALUE, "this call needs routed experts (n_routed >= 1)");
   return MOE_OK;
 }
 
@@ -81,13 +93,16 @@ static moe_status check_ws(const moe_dims &dm, int64_t T, const void *ws, size_t
 
 static moe_status check_weights(const moe_dims &dm, const moe_weights *w, bool need_router, bool need_experts) {
   if (!w) return fail(MOE_ERR_INVALID_VALUE, "weights is NULL");
-  if (need_router) MOE_CHECK(check_ptr(w->w_router, "w_router"));
+  const bool dense = dm.n_routed == 0;
+  if (need_router && !dense) MOE_CHECK(check_ptr(w->w_router, "w_router"));
   if (w->router_bias && ((uintptr_t)w->router_bias & 3u))
     return fail(MOE_ERR_INVALID_VALUE, "router_bias is not 4-byte aligned");
   if (need_experts) {
-    MOE_CHECK(check_ptr(w->w1, "w1"));
-    MOE_CHECK(check_ptr(w->w3, "w3"));
-    MOE_CHECK(check_ptr(w->w2, "w2"));
+    if (!dense) {
+      MOE_CHECK(check_ptr(w->w1, "w1"));
+      MOE_CHECK(check_ptr(w->w3, "w3"));
+      MOE_CHECK(check_ptr(w->w2, "w2"));
+    }
     if (dm.d_ff_shared > 0) {
       MOE_CHECK(check_ptr(w->w1s, "w1s"));
       MOE_CHECK(check_ptr(w->w3s, "w3s"));
@@ -106,20 +121,28 @@ static moe_status check_opts(const moe_options *o) {
   return MOE_OK;
 }
 
-// Which expert-FFN kernels run: 1 prefill, 2 decode.
+// Which expert-FFN kernels run: 1 prefill, 2 decode.  A dense layer streams
+// its single weight set per 16 rows on the decode path, so it switches to the
+// tiled GEMMs at a smaller T than a routed layer, whose experts see about
+// T*k/N_r rows each.
 static int pick_path(const moe_dims &dm, int64_t T, const moe_options *o) {
   const int want = o ? o->path : 0;
   if (want != 0) return want;
+  if (dm.n_routed == 0) return T <= 64 ? 2 : 1;
   return (T * dm.top_k <= 2 * (int64_t)dm.n_routed && T <= 256) ? 2 : 1;
 }
 
+// Records events[base + i] at stage boundary i (when the caller gave it).
 struct EventHook {
   const moe_options *o;
   hipStream_t st;
+  int base = 0;
   void rec(int i) const {
+    i += base;
     if (o && o->events && i < o->n_events && o->events[i]) (void)hipEventRecord((hipEvent_t)o->events[i], st);
   }
   hipEvent_t get(int i) const {
+    i += base;
     return (o && o->events && i < o->n_events) ? (hipEvent_t)o->events[i] : nullptr;
   }
 };
@@ -157,6 +180,57 @@ static moe_status run_ffn(const moe_dims &dm, int64_t T, const void *u, const mo
   return MOE_OK;
 }
 
+static moe_status check_eps(double eps) {
+  if (!(eps >= 0.0) || eps == __builtin_inf()) return fail(MOE_ERR_INVALID_VALUE, "eps must be finite and >= 0");
+  return MOE_OK;
+}
+
+// the byte ranges [a, a + na) and [b, b + nb) must not overlap
+static moe_status check_no_overlap(const void *a, size_t na, const void *b, size_t nb, const char *name) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  if (pa < pb + nb && pb < pa + na) return fail(MOE_ERR_INVALID_VALUE, "%s overlaps x", name);
+  return MOE_OK;
+}
+
+static size_t td_bytes(const moe_dims &dm, int64_t T, int dtype) {
+  return (size_t)T * dm.d_model * (dtype == MOE_BF16 ? 2 : 4);
+}
+
+// Router, permutation, expert FFNs and combine on the (validated) input u;
+// resid (NULL or the block input x) is added in the combine.  Stage events
+// 1..6 as in moe_layer_forward (relative to ev.base); a dense layer has no
+// routing stages and records 1..3 at the same point.
+static moe_status run_layer(const moe_dims &dm, int64_t T, const void *u, const moe_weights &wts, const void *resid,
+                            void *out, const moe_options *opts, const WsLayout &L, char *w, hipStream_t st,
+                            const EventHook &ev) {
+  int32_t *idx = (int32_t *)(w + L.topk_idx);
+  float *gw = (float *)(w + L.topk_w);
+  int32_t *counts = (int32_t *)(w + L.counts);
+  int32_t *offsets = (int32_t *)(w + L.offsets);
+  int32_t *row_token = (int32_t *)(w + L.row_token);
+  int32_t *token_row = (int32_t *)(w + L.token_row);
+  float *y_rows = (float *)(w + L.y_rows);
+  float *y_sh = dm.d_ff_shared > 0 ? (float *)(w + L.y_sh) : nullptr;
+  MOE_TRY_HIP(launch_diag_clear(w, st), "diag clear");
+  if (dm.n_routed > 0) {
+    MOE_TRY_HIP(launch_router_logits(dm, T, u, wts.w_router, wts.router_bias, L, w, st), "router logits");
+    ev.rec(1);
+    MOE_TRY_HIP(launch_topk(dm, T, u, wts.w_router, wts.router_bias, idx, gw, L, w, st), "top-k");
+    ev.rec(2);
+    MOE_TRY_HIP(launch_permute(dm, T, idx, counts, offsets, row_token, token_row, L, w, st), "permute");
+  } else {
+    ev.rec(1);
+    ev.rec(2);
+  }
+  MOE_TRY_HIP(launch_tile_offsets(dm, T, counts, L, w, st), "tile offsets");
+  ev.rec(3);
+  MOE_CHECK(run_ffn(dm, T, u, wts, counts, offsets, row_token, y_rows, y_sh, opts, L, w, st, ev.get(4)));
+  ev.rec(5);
+  MOE_TRY_HIP(launch_combine(dm, T, y_rows, y_sh, gw, token_row, resid, out, st), "combine");
+  ev.rec(6);
+  return MOE_OK;
+}
+
 extern "C" {
 
 const char *moe_last_error(void) { return g_err; }
@@ -172,6 +246,7 @@ moe_status moe_router_topk(const moe_dims *dims, int64_t T, const void *u, const
                            const float *router_bias, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
                            void *stream) {
   MOE_CHECK(check_dims(dims, T));
+  MOE_CHECK(need_routed(*dims));
   if (T == 0) return MOE_OK;
   MOE_CHECK(check_ptr(u, "u"));
   MOE_CHECK(check_ptr(w_router, "w_router"));
@@ -191,6 +266,7 @@ moe_status moe_router_topk(const moe_dims *dims, int64_t T, const void *u, const
 moe_status moe_permute(const moe_dims *dims, int64_t T, const int32_t *topk_idx, int32_t *counts, int32_t *offsets,
                        int32_t *row_token, int32_t *token_row, void *ws, size_t ws_bytes, void *stream) {
   MOE_CHECK(check_dims(dims, T));
+  MOE_CHECK(need_routed(*dims));
   if (T == 0) return MOE_OK;
   MOE_CHECK(check_ptr(topk_idx, "topk_idx"));
   MOE_CHECK(check_ptr(counts, "counts"));
@@ -214,10 +290,16 @@ moe_status moe_expert_ffn(const moe_dims *dims, int64_t T, const void *u, const 
   if (T == 0) return MOE_OK;
   MOE_CHECK(check_ptr(u, "u"));
   MOE_CHECK(check_weights(*dims, wts, false, true));
-  MOE_CHECK(check_ptr(counts, "counts"));
-  MOE_CHECK(check_ptr(offsets, "offsets"));
-  MOE_CHECK(check_ptr(row_token, "row_token"));
-  MOE_CHECK(check_ptr(y_rows, "y_rows"));
+  if (dims->n_routed > 0) {
+    MOE_CHECK(check_ptr(counts, "counts"));
+    MOE_CHECK(check_ptr(offsets, "offsets"));
+    MOE_CHECK(check_ptr(row_token, "row_token"));
+    MOE_CHECK(check_ptr(y_rows, "y_rows"));
+  } else {
+    counts = offsets = nullptr;
+    row_token = nullptr;
+    y_rows = nullptr;
+  }
   if (dims->d_ff_shared > 0) MOE_CHECK(check_ptr(y_shared, "y_shared"));
   else if (y_shared) return fail(MOE_ERR_INVALID_VALUE, "y_shared given but d_ff_shared == 0");
   WsLayout L;
@@ -237,12 +319,19 @@ moe_status moe_combine(const moe_dims *dims, int64_t T, const float *y_rows, con
                        const float *topk_w, const int32_t *token_row, void *out, void *stream) {
   MOE_CHECK(check_dims(dims, T));
   if (T == 0) return MOE_OK;
-  MOE_CHECK(check_ptr(y_rows, "y_rows"));
-  if (y_shared) MOE_CHECK(check_ptr(y_shared, "y_shared"));
-  MOE_CHECK(check_ptr(topk_w, "topk_w"));
-  MOE_CHECK(check_ptr(token_row, "token_row"));
+  if (dims->top_k > 0) {
+    MOE_CHECK(check_ptr(y_rows, "y_rows"));
+    if (y_shared) MOE_CHECK(check_ptr(y_shared, "y_shared"));
+    MOE_CHECK(check_ptr(topk_w, "topk_w"));
+    MOE_CHECK(check_ptr(token_row, "token_row"));
+  } else {
+    MOE_CHECK(check_ptr(y_shared, "y_shared"));
+    y_rows = topk_w = nullptr;
+    token_row = nullptr;
+  }
   MOE_CHECK(check_ptr(out, "out"));
-  MOE_TRY_HIP(launch_combine(*dims, T, y_rows, y_shared, topk_w, token_row, out, (hipStream_t)stream), "combine");
+  MOE_TRY_HIP(launch_combine(*dims, T, y_rows, y_shared, topk_w, token_row, nullptr, out, (hipStream_t)stream),
+              "combine");
   return MOE_OK;
 }
 
@@ -257,32 +346,48 @@ moe_status moe_layer_forward(const moe_dims *dims, int64_t T, const void *u, con
   WsLayout L;
   MOE_CHECK(check_ws(*dims, T, ws, ws_bytes, &L));
   MOE_CHECK(check_path_limits(*dims, T, opts));
-  const moe_dims &dm = *dims;
   hipStream_t st = (hipStream_t)stream;
-  char *w = (char *)ws;
-  int32_t *idx = (int32_t *)(w + L.topk_idx);
-  float *gw = (float *)(w + L.topk_w);
-  int32_t *counts = (int32_t *)(w + L.counts);
-  int32_t *offsets = (int32_t *)(w + L.offsets);
-  int32_t *row_token = (int32_t *)(w + L.row_token);
-  int32_t *token_row = (int32_t *)(w + L.token_row);
-  float *y_rows = (float *)(w + L.y_rows);
-  float *y_sh = dm.d_ff_shared > 0 ? (float *)(w + L.y_sh) : nullptr;
   EventHook ev{opts, st};
   ev.rec(0);
-  MOE_TRY_HIP(launch_diag_clear(w, st), "diag clear");
-  MOE_TRY_HIP(launch_router_logits(dm, T, u, wts->w_router, wts->router_bias, L, w, st), "router logits");
-  ev.rec(1);
-  MOE_TRY_HIP(launch_topk(dm, T, u, wts->w_router, wts->router_bias, idx, gw, L, w, st), "top-k");
-  ev.rec(2);
-  MOE_TRY_HIP(launch_permute(dm, T, idx, counts, offsets, row_token, token_row, L, w, st), "permute");
-  MOE_TRY_HIP(launch_tile_offsets(dm, T, counts, L, w, st), "tile offsets");
-  ev.rec(3);
-  MOE_CHECK(run_ffn(dm, T, u, *wts, counts, offsets, row_token, y_rows, y_sh, opts, L, w, st, ev.get(4)));
-  ev.rec(5);
-  MOE_TRY_HIP(launch_combine(dm, T, y_rows, y_sh, gw, token_row, out, st), "combine");
-  ev.rec(6);
+  return run_layer(*dims, T, u, *wts, nullptr, out, opts, L, (char *)ws, st, ev);
+}
+
+moe_status moe_rmsnorm(const moe_dims *dims, int64_t T, const void *x, const float *norm_weight, double eps, void *u,
+                       void *stream) {
+  MOE_CHECK(check_dims(dims, T));
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(check_ptr(x, "x"));
+  MOE_CHECK(check_ptr(norm_weight, "norm_weight"));
+  MOE_CHECK(check_ptr(u, "u"));
+  MOE_CHECK(check_eps(eps));
+  MOE_CHECK(check_no_overlap(x, td_bytes(*dims, T, dims->dtype), u, td_bytes(*dims, T, dims->dtype), "u"));
+  MOE_TRY_HIP(launch_rmsnorm(*dims, T, x, norm_weight, eps, u, (hipStream_t)stream), "rmsnorm");
   return MOE_OK;
+}
+
+moe_status moe_block_forward(const moe_dims *dims, int64_t T, const void *x, const float *norm_weight, double eps,
+                             const moe_weights *wts, void *out, const moe_options *opts, void *ws, size_t ws_bytes,
+                             void *stream) {
+  MOE_CHECK(check_dims(dims, T));
+  MOE_CHECK(check_opts(opts));
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(check_ptr(x, "x"));
+  MOE_CHECK(check_ptr(norm_weight, "norm_weight"));
+  MOE_CHECK(check_eps(eps));
+  MOE_CHECK(check_weights(*dims, wts, true, true));
+  MOE_CHECK(check_ptr(out, "out"));
+  WsLayout L;
+  MOE_CHECK(check_ws(*dims, T, ws, ws_bytes, &L));
+  MOE_CHECK(check_path_limits(*dims, T, opts));
+  MOE_CHECK(check_no_overlap(x, td_bytes(*dims, T, dims->dtype), out, td_bytes(*dims, T, dims->out_dtype), "out"));
+  hipStream_t st = (hipStream_t)stream;
+  char *w = (char *)ws;
+  void *u = w + L.u_norm;
+  EventHook ev{opts, st};
+  ev.rec(0);
+  MOE_TRY_HIP(launch_rmsnorm(*dims, T, x, norm_weight, eps, u, st), "rmsnorm");
+  ev.base = 1;
+  return run_layer(*dims, T, u, *wts, x, out, opts, L, w, st, ev);
 }
 
 moe_status moe_read_diagnostics(const void *ws, moe_diag *diag, void *stream) {

@@ -9,10 +9,15 @@
 // Three launches, no atomics on the global result:
 //   1. per block of 256 tokens, an LDS bitmap per expert (bit i = token i of the
 //      block chose the expert); its popcount is the block's count per expert;
-//   2. one work-group: per-expert totals, the exclusive scan over experts
-//      (offsets), and each block's starting row per expert;
+//   2. one work-group: per-expert totals, the seats each expert keeps (all of
+//      its pairs, or at most the capacity), the exclusive scan of the kept
+//      counts over experts (offsets), and each block's first rank per expert;
 //   3. per block, rebuild the bitmap; a token's rank inside its expert group is
-//      the popcount of the bits below it, so rows follow token order.
+//      the popcount of the bits below it, so rows follow token order, and a
+//      pair whose rank reaches the capacity is dropped (token_row -1).
+// The capacity rule is "What is an 'expert', really?" (glossary: capacity
+// factor / token dropping: a seat limit per expert, overflow skipped), read as
+// "each expert keeps its first seats in token order".
 #include "common.h"
 
 #define PERM_WORDS (MOE_PERM_BLOCK / 64)
@@ -69,7 +74,8 @@ __device__ int block_exclusive_scan(int v, int *sh, int *total) {
   return incl - v;
 }
 
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ blk_hist, int64_t nblk, int E,
+// cap: seats per expert, 0 = no limit
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ blk_hist, int64_t nblk, int E, int cap,
                                                          int32_t *__restrict__ counts, int32_t *__restrict__ offsets) {
   __shared__ int sh[1024];
   const int e = threadIdx.x;
@@ -77,23 +83,24 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ b
   if (e < E) {
     for (int64_t b = 0; b < nblk; ++b) {
       const int c = blk_hist[b * E + e];
-      blk_hist[b * E + e] = tot;  // exclusive within the expert
+      blk_hist[b * E + e] = tot;  // the expert's pairs in earlier blocks: the block's first rank
       tot += c;
     }
   }
+  const int seats = (cap > 0 && tot > cap) ? cap : tot;
   int all;
-  const int off = block_exclusive_scan(e < E ? tot : 0, sh, &all);
+  const int off = block_exclusive_scan(e < E ? seats : 0, sh, &all);
   if (e < E) {
-    counts[e] = tot;
+    counts[e] = seats;
     offsets[e] = off;
-    for (int64_t b = 0; b < nblk; ++b) blk_hist[b * E + e] += off;
   }
   if (e == 0) offsets[E] = all;
 }
 
 __global__ __launch_bounds__(MOE_PERM_BLOCK) void perm_scatter_kernel(const int32_t *__restrict__ idx, int64_t T,
-                                                                      int E, int k,
+                                                                      int E, int k, int cap,
                                                                       const int32_t *__restrict__ blk_base,
+                                                                      const int32_t *__restrict__ offsets,
                                                                       int32_t *__restrict__ row_token,
                                                                       int32_t *__restrict__ token_row) {
   extern __shared__ unsigned long long bm[];
@@ -115,7 +122,12 @@ __global__ __launch_bounds__(MOE_PERM_BLOCK) void perm_scatter_kernel(const int3
       if (q < w) rank += __popcll(row[q]);
     const unsigned long long below = (i & 63) ? (row[w] & ((1ull << (i & 63)) - 1ull)) : 0ull;
     rank += __popcll(below);
-    const int r = blk_base[(int64_t)blockIdx.x * E + e] + rank;
+    rank += blk_base[(int64_t)blockIdx.x * E + e];  // rank among all of the expert's pairs
+    if (cap > 0 && rank >= cap) {
+      token_row[t * k + j] = -1;  // no seat left
+      continue;
+    }
+    const int r = offsets[e] + rank;
     token_row[t * k + j] = r;
     row_token[r] = (int32_t)t;
   }
@@ -129,9 +141,9 @@ hipError_t launch_permute(const moe_dims &dm, int64_t T, const int32_t *topk_idx
   DiagWords *diag = (DiagWords *)(ws + L.diag);
   const size_t lds = (size_t)E * PERM_WORDS * sizeof(unsigned long long);
   perm_hist_kernel<<<dim3((unsigned)nblk), MOE_PERM_BLOCK, lds, st>>>(topk_idx, T, E, k, blk, diag);
-  perm_scan_kernel<<<1, 1024, 0, st>>>(blk, nblk, E, counts, offsets);
-  perm_scatter_kernel<<<dim3((unsigned)nblk), MOE_PERM_BLOCK, lds, st>>>(topk_idx, T, E, k, blk, row_token,
-                                                                          token_row);
+  perm_scan_kernel<<<1, 1024, 0, st>>>(blk, nblk, E, dm.capacity, counts, offsets);
+  perm_scatter_kernel<<<dim3((unsigned)nblk), MOE_PERM_BLOCK, lds, st>>>(topk_idx, T, E, k, dm.capacity, blk,
+                                                                          offsets, row_token, token_row);
   return hipGetLastError();
 }
 

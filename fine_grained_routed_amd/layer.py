@@ -12,34 +12,41 @@ _DT = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
 
 
 class MoELayer:
-    """One shared + routed MoE FFN layer whose weights live on the GPU.
+    """One shared + routed MoE FFN layer (or a dense FFN layer) whose weights live on the GPU.
 
     weights: dict with w_router [N_r,d], w1/w3 [N_r,f,d], w2 [N_r,d,f],
-    optional w1s/w3s [f_s,d], w2s [d,f_s] and router_bias [N_r] fp32.
+    optional w1s/w3s [f_s,d], w2s [d,f_s] and router_bias [N_r] fp32.  A dense
+    layer has top_k == 0 and no routed experts (w_router None or with 0 rows);
+    its MLP is w1s/w3s/w2s.  capacity: seats per routed expert (0 = no limit).
     """
 
     def __init__(self, weights: Dict[str, Optional[torch.Tensor]], top_k: int, out_dtype=torch.float32,
-                 lib: Optional[Library] = None):
+                 lib: Optional[Library] = None, capacity: int = 0):
         self.lib = lib or load()
         self.w = weights
-        wr, w1 = weights["w_router"], weights["w1"]
         for name, t in weights.items():
             if t is not None and not t.is_contiguous():
                 raise ValueError(f"{name} must be contiguous")
-        self.E, self.d = wr.shape
-        self.f = w1.shape[1]
-        self.fs = 0 if weights.get("w1s") is None else weights["w1s"].shape[0]
+        wr, w1, w1s = weights.get("w_router"), weights.get("w1"), weights.get("w1s")
+        ref = w1s if wr is None or wr.shape[0] == 0 else wr
+        self.E = 0 if wr is None else wr.shape[0]
+        self.d = ref.shape[1]
+        self.f = 0 if w1 is None or self.E == 0 else w1.shape[1]
+        self.fs = 0 if w1s is None else w1s.shape[0]
         self.k = top_k
-        self.dtype = wr.dtype
+        self.dtype = ref.dtype
         self.out_dtype = out_dtype
-        self.dims = self.lib.dims(self.d, self.E, self.f, self.fs, top_k, _DT[wr.dtype], _DT[out_dtype])
-        self.cw = self.lib.weights(wr, weights.get("router_bias"), w1, weights["w3"], weights["w2"],
-                                   weights.get("w1s"), weights.get("w3s"), weights.get("w2s"))
+        self.capacity = capacity
+        self.dims = self.lib.dims(self.d, self.E, self.f, self.fs, top_k, _DT[ref.dtype], _DT[out_dtype], capacity)
+        routed = self.E > 0
+        self.cw = self.lib.weights(wr if routed else None, weights.get("router_bias") if routed else None,
+                                   w1 if routed else None, weights.get("w3") if routed else None,
+                                   weights.get("w2") if routed else None, w1s, weights.get("w3s"), weights.get("w2s"))
         self._ws = None
 
     @property
     def device(self):
-        return self.w["w_router"].device
+        return next(t for t in self.w.values() if t is not None).device
 
     def workspace(self, T: int) -> torch.Tensor:
         need = self.lib.workspace_size(self.dims, T)
@@ -58,6 +65,22 @@ class MoELayer:
         return out
 
     __call__ = forward
+
+    def block_forward(self, x: torch.Tensor, norm_weight: torch.Tensor, eps: float,
+                      out: Optional[torch.Tensor] = None, path: int = PATH_AUTO,
+                      events: Optional[Sequence[int]] = None) -> torch.Tensor:
+        """Pre-norm block: x + layer(RMSNorm(x)); norm_weight [d] fp32."""
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((T, self.d), dtype=self.out_dtype, device=self.device)
+        ws = self.workspace(T)
+        self.lib.block_forward(self.dims, T, x, norm_weight, eps, self.cw, out, self.lib.options(path, events), ws)
+        return out
+
+    def rmsnorm(self, x: torch.Tensor, norm_weight: torch.Tensor, eps: float) -> torch.Tensor:
+        u = torch.empty_like(x)
+        self.lib.rmsnorm(self.dims, x.shape[0], x, norm_weight, eps, u)
+        return u
 
     def diagnostics(self) -> dict:
         return self.lib.read_diagnostics(self._ws)
@@ -90,10 +113,10 @@ class MoELayer:
         return y_rows, y_sh
 
     def combine(self, y_rows, y_shared, topk_w, token_row, out_dtype=None):
-        T = topk_w.shape[0]
+        T = (topk_w if topk_w is not None else y_shared).shape[0]
         out = torch.empty((T, self.d), dtype=out_dtype or self.out_dtype, device=self.device)
         dims = self.dims
         if out_dtype is not None and _DT[out_dtype] != dims.out_dtype:
-            dims = self.lib.dims(self.d, self.E, self.f, self.fs, self.k, dims.dtype, _DT[out_dtype])
+            dims = self.lib.dims(self.d, self.E, self.f, self.fs, self.k, dims.dtype, _DT[out_dtype], self.capacity)
         self.lib.combine(dims, T, y_rows, y_shared, topk_w, token_row, out)
         return out

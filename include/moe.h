@@ -17,9 +17,22 @@
  *   FFN(x)  = W2 (SiLU(W1 x) * W3 x),   SiLU(z) = z * sigmoid(z)
  *
  * The kept gates are NOT renormalised; the shared MLP enters with coefficient
- * exactly 1; no residual is added and no normalisation is applied (u arrives
- * already RMS-normalised).  Every token goes to all k of its experts (no
- * capacity limit).
+ * exactly 1; moe_layer_forward adds no residual and applies no normalisation
+ * (u arrives already RMS-normalised).  moe_block_forward is the pre-norm block
+ * around it: u = RMSNorm(x), out = x + layer(u).
+ *
+ * Every token goes to all k of its experts unless moe_dims.capacity sets a
+ * seat limit per expert: then each expert keeps the first `capacity` of its
+ * (token, slot) pairs in token order and the rest are dropped (they contribute
+ * nothing; the shared MLP still runs on every token).  Source: "What is an
+ * 'expert', really?", glossary: capacity factor / token dropping.
+ *
+ * Dense layers: n_routed == 0 (with top_k == 0) describes the dense prefix
+ * layers' feed-forward block ("Shared and fine-grained experts", Developer
+ * level: the first three DeepSeek-V3 layers stay dense, width 18432; "Shared
+ * Expert", Official code: the same SwiGLU as the shared MLP).  Only the MLP of
+ * width d_ff_shared (> 0) runs, through the shared-group kernels:
+ *   out[t] = W2s (SiLU(W1s u[t]) * W3s u[t]);  d_ff, w_router, w1, w3, w2 are ignored.
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless marked (host).  Every array is dense,
@@ -38,7 +51,8 @@
  *     message in moe_last_error().  T == 0 is a valid no-op.
  *   - Faults inside a kernel surface at the caller's next synchronisation.
  *
- * Limits: 1 <= top_k <= 16; 1 <= n_routed <= 1024; top_k <= n_routed;
+ * Limits: 1 <= top_k <= 16; 1 <= n_routed <= 1024; top_k <= n_routed (or
+ * n_routed == top_k == 0 for a dense layer); capacity >= 0;
  * d_model and d_ff (and d_ff_shared when non-zero) multiples of 64;
  * 64 <= d_model <= 32768; T * top_k < 2^31.  On the bf16 prefill path every
  * matrix the expert GEMMs read (u, the [T*k, f] and [T, f_s] hidden
@@ -76,6 +90,8 @@ typedef struct moe_dims {
   int32_t top_k;       /* k */
   int32_t dtype;       /* moe_dtype of u and the weights */
   int32_t out_dtype;   /* moe_dtype of `out` (MOE_F32 recommended) */
+  int32_t capacity;    /* seats per routed expert per call; 0 = no limit.  A caller
+                          with a capacity factor cf uses ceil(cf * T * top_k / n_routed). */
 } moe_dims;
 
 /* Device pointers to the layer's weights (layouts above).  router_bias may be
@@ -94,9 +110,12 @@ typedef struct moe_weights {
  *   events (host array of n_events hipEvent_t, may be NULL): when non-NULL the
  *   library records events[i] on `stream` at stage boundaries, in this order:
  *   0 start, 1 after router logits, 2 after top-k, 3 after permutation,
- *   4 after gate/up, 5 after down, 6 after combine (moe_layer_forward), or
- *   0 start, 1 after gate/up, 2 after down (moe_expert_ffn).  Boundaries
- *   beyond n_events are not recorded. */
+ *   4 after gate/up, 5 after down, 6 after combine (moe_layer_forward; for a
+ *   dense layer 1-3 mark the same point), or 0 start, 1 after RMSNorm, then
+ *   2..7 as 1..6 above (moe_block_forward), or 0 start, 1 after gate/up,
+ *   2 after down (moe_expert_ffn).  Boundaries beyond n_events are not
+ *   recorded.
+ *   The automatic choice for a dense layer is the decode path when T <= 64. */
 typedef struct moe_options {
   int32_t path;
   int32_t n_events;
@@ -116,7 +135,7 @@ typedef struct moe_diag {
 /* Workspace needed by every call below for this shape and token count (host out). */
 moe_status moe_workspace_size(const moe_dims *dims, int64_t T, size_t *bytes);
 
-/* Router: logits, softmax over all N_r experts, per-token top-k.
+/* Router: logits, softmax over all N_r experts, per-token top-k (n_routed >= 1).
  * Writes topk_idx [T, k] int32 (slot 0 = largest logit; ties to the lower
  * expert index; the selection and slot order equal those of the exact real
  * logits of the stored inputs) and topk_w [T, k] fp32 = the full-softmax
@@ -128,12 +147,17 @@ moe_status moe_router_topk(const moe_dims *dims, int64_t T, const void *u, const
                            void *ws, size_t ws_bytes, void *stream);
 
 /* Permutation: group the T*k (token, slot) pairs by expert.
- * counts [N_r] = pairs per expert; offsets [N_r+1] exclusive prefix of counts
- * (offsets[N_r] = T*k); row_token [T*k]: rows offsets[e]..offsets[e+1]-1 hold
- * the tokens that chose e in ascending token order; token_row [T, k]: the row
- * of token t's slot j.  Deterministic and bit-exact.  Each row of topk_idx must
- * hold k distinct experts in [0, N_r); violations set moe_diag.flags.
- * Source: "Shared Expert" (How it works: scatter-sum of routed outputs). */
+ * counts [N_r] = pairs kept per expert; offsets [N_r+1] exclusive prefix of
+ * counts (offsets[N_r] = T*k without a capacity); row_token [T*k]: rows
+ * offsets[e]..offsets[e+1]-1 hold the tokens that chose e in ascending token
+ * order; token_row [T, k]: the row of token t's slot j, or -1 when the pair was
+ * dropped for capacity.  With dims->capacity = C > 0, counts[e] = min(pairs, C)
+ * and expert e keeps its first C pairs in token order; row_token entries
+ * past offsets[N_r] are then left unwritten.  Deterministic and
+ * bit-exact.  Each row of topk_idx must hold k distinct experts in [0, N_r);
+ * violations set moe_diag.flags.  Needs n_routed >= 1.
+ * Source: "Shared Expert" (How it works: scatter-sum of routed outputs);
+ * "What is an 'expert', really?" (glossary: capacity factor / token dropping). */
 moe_status moe_permute(const moe_dims *dims, int64_t T, const int32_t *topk_idx, int32_t *counts,
                        int32_t *offsets, int32_t *row_token, int32_t *token_row,
                        void *ws, size_t ws_bytes, void *stream);
@@ -144,16 +168,20 @@ moe_status moe_permute(const moe_dims *dims, int64_t T, const int32_t *topk_idx,
  * counts/offsets/row_token are moe_permute's outputs.
  * Source: "Shared Expert" (How it works: SwiGLU; Official code: fused shared
  * MLP of width N_s*f on the full batch); "Shared and fine-grained experts"
- * (Researcher level, Systems limits: grouped GEMM over many small experts). */
+ * (Researcher level, Systems limits: grouped GEMM over many small experts).
+ * Dense layer (n_routed == 0): only y_shared is written; counts, offsets,
+ * row_token and y_rows are ignored and may be NULL. */
 moe_status moe_expert_ffn(const moe_dims *dims, int64_t T, const void *u, const moe_weights *w,
                           const int32_t *counts, const int32_t *offsets, const int32_t *row_token,
                           float *y_rows, float *y_shared, const moe_options *opts,
                           void *ws, size_t ws_bytes, void *stream);
 
 /* Combine: out[t,:] = y_shared[t,:] + sum_{j=0..k-1} topk_w[t,j] * y_rows[token_row[t,j],:],
- * accumulated in fp32 in exactly this order (y_shared NULL: start from 0),
- * written as out_dtype.  Source: "Shared Expert" (How it works: shared output
- * added to the scatter-sum of routed outputs; Watch-outs: coefficient 1). */
+ * accumulated in fp32 in exactly this order (y_shared NULL: start from 0;
+ * slots with token_row -1 skipped), written as out_dtype.  Dense layer
+ * (top_k == 0): out = y_shared converted; y_rows, topk_w, token_row ignored.
+ * Source: "Shared Expert" (How it works: shared output added to the
+ * scatter-sum of routed outputs; Watch-outs: coefficient 1). */
 moe_status moe_combine(const moe_dims *dims, int64_t T, const float *y_rows, const float *y_shared,
                        const float *topk_w, const int32_t *token_row, void *out, void *stream);
 
@@ -161,6 +189,29 @@ moe_status moe_combine(const moe_dims *dims, int64_t T, const float *y_rows, con
  * out_dtype receives shared + routed (no residual).  Intermediates live in ws. */
 moe_status moe_layer_forward(const moe_dims *dims, int64_t T, const void *u, const moe_weights *w,
                              void *out, const moe_options *opts, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* RMSNorm of the residual stream: u[t,:] = x[t,:] / sqrt(mean_c x[t,c]^2 + eps) * norm_weight[:].
+ * x and u are [T, d_model] in dims->dtype; norm_weight [d_model] is fp32.
+ * The mean of squares, the scale and the products are evaluated in fp64 and
+ * rounded once to dims->dtype (to nearest, ties to even), so u matches the
+ * exact normalisation rounded once, except for a value within an fp64 ulp of
+ * a rounding midpoint.  eps >= 0.  u may not alias x.  Only dims->d_model and
+ * dims->dtype are read.
+ * Source: "Shared Expert" (How it works: the FFN input is already
+ * RMS-normalised; Watch-outs: the shared experts sit behind ffn_norm). */
+moe_status moe_rmsnorm(const moe_dims *dims, int64_t T, const void *x, const float *norm_weight, double eps,
+                       void *u, void *stream);
+
+/* Pre-norm block: u = RMSNorm(x) (as moe_rmsnorm, kept in ws), then the layer
+ * on u (as moe_layer_forward), then out[t,:] = x[t,:] + layer(u)[t,:], the
+ * residual added in fp32 after the layer's own fp32 sum, written as
+ * out_dtype.  x [T, d_model] in dtype; out may not alias x.  Works for dense
+ * layers (n_routed == 0) too.
+ * Source: "Shared Expert" (How it works: eq. 12's residual is added at block
+ * level, x = x + ffn(ffn_norm(x)); MoE.forward returns shared + routed only). */
+moe_status moe_block_forward(const moe_dims *dims, int64_t T, const void *x, const float *norm_weight, double eps,
+                             const moe_weights *w, void *out, const moe_options *opts, void *ws, size_t ws_bytes,
                              void *stream);
 
 /* Copy the diagnostics of the last call that used `ws` to *diag (host);

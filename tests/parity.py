@@ -69,12 +69,29 @@ def run_stages(layer, u, path: int):
                 out_stages=out_stages, routed=routed, out=out, diag=diag)
 
 
+def oracle_outputs(u64, toks, a, k, idx_o, token_row_o, capacity):
+    """Oracle layer output and routed-only part for the tokens toks.  With a
+    capacity, which pairs keep a seat depends on the whole batch: the kept mask
+    comes from the oracle's permutation of all tokens, and a dropped pair's gate
+    is zeroed (its expert output then adds exactly nothing)."""
+    r = oracle.forward(u64[toks], a["w_router"], a["w1"], a["w3"], a["w2"], k, a["bias"],
+                       a["w1s"], a["w3s"], a["w2s"])
+    assert np.array_equal(r["topk_idx"], idx_o[toks])
+    if not capacity:
+        return r["out"], r["routed"]
+    gates = r["topk_w"] * (token_row_o[toks] >= 0)
+    return (oracle.combine(r["y_rows"], r["y_shared"], gates, r["token_row"]),
+            oracle.combine(r["y_rows"], None, gates, r["token_row"]))
+
+
 def check_case(layer, inp, wl: workloads.Workload, path: int = 0, sample: Optional[int] = None, seed: int = 0):
     """Full parity check of one case.  sample=None compares every token's output;
-    otherwise routing is compared on all tokens and outputs on a seeded sample."""
+    otherwise routing is compared on all tokens and outputs on a seeded sample.
+    A layer built with a capacity is checked against the oracle's capacity rule."""
     u = inp["u"]
     T = u.shape[0]
-    log(f"[parity] {wl.name} T={T} path={path} sample={sample}")
+    cap = getattr(layer, "capacity", 0) or None
+    log(f"[parity] {wl.name} T={T} path={path} sample={sample} capacity={cap}")
     g = run_stages(layer, u, path)
     a = oracle_args(inp)
     u64 = workloads.to_f64(u)
@@ -86,26 +103,26 @@ def check_case(layer, inp, wl: workloads.Workload, path: int = 0, sample: Option
                            f"oracle {idx_o[bad[:3]]}; diagnostics {g['diag']}")
     gerr = float(np.max(np.abs(g["gw"].cpu().numpy().astype(np.float64) - gw_o)))
     assert gerr <= GATE_TOL, f"gate error {gerr}"
-    counts_o, offsets_o, row_token_o, token_row_o = oracle.permute(idx_o, wl.n_routed)
+    counts_o, offsets_o, row_token_o, token_row_o = oracle.permute(idx_o, wl.n_routed, cap)
     assert np.array_equal(g["counts"].cpu().numpy(), counts_o)
     assert np.array_equal(g["offsets"].cpu().numpy(), offsets_o)
-    assert np.array_equal(g["row_token"].cpu().numpy(), row_token_o)
+    # rows past offsets[N_r] exist only when pairs were dropped, and are left unwritten
+    assert np.array_equal(g["row_token"].cpu().numpy()[:offsets_o[-1]], row_token_o)
     assert np.array_equal(g["token_row"].cpu().numpy(), token_row_o)
     assert g["diag"]["flags"] == 0, g["diag"]
     # -- the fused call equals the stage-by-stage calls bit for bit
     assert torch.equal(g["out"], g["out_stages"])
     # -- outputs
     toks = np.arange(T) if sample is None else workloads.sample_tokens(T, sample, seed)
-    r = oracle.forward(u64[toks], a["w_router"], a["w1"], a["w3"], a["w2"], wl.top_k, a["bias"],
-                       a["w1s"], a["w3s"], a["w2s"])
-    assert np.array_equal(r["topk_idx"], idx_o[toks])
+    want_out, want_routed = oracle_outputs(u64, toks, a, wl.top_k, idx_o, token_row_o, cap)
     out_g = g["out"][torch.from_numpy(toks).to(u.device)].to(torch.float64).cpu().numpy()
     routed_g = g["routed"][torch.from_numpy(toks).to(u.device)].to(torch.float64).cpu().numpy()
-    e_out = rel_err(out_g, r["out"])
-    e_routed = rel_err_per_token(routed_g, r["routed"])
+    e_out = rel_err(out_g, want_out)
+    e_routed = rel_err_per_token(routed_g, want_routed)
     tol = TOL[wl.dtype]
     log(f"[parity] {wl.name} T={T}: out err {e_out:.3e}, routed-only err {e_routed:.3e}, gate err {gerr:.2e}, "
         f"exact-ranked tokens gpu {g['diag']['tokens_exact']} oracle {n_exact}")
     assert e_out <= tol, f"output error {e_out} > {tol}"
     assert e_routed <= tol, f"routed-only output error (per token) {e_routed} > {tol}"
-    return dict(out_err=e_out, routed_err=e_routed, gate_err=gerr, diag=g["diag"], out=g["out"])
+    return dict(out_err=e_out, routed_err=e_routed, gate_err=gerr, diag=g["diag"], out=g["out"],
+                dropped=int((token_row_o < 0).sum()))

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_struct_sizes_match_header():
-    assert ctypes.sizeof(B.Dims) == 28
+    assert ctypes.sizeof(B.Dims) == 32
     assert ctypes.sizeof(B.Weights) == 64
     assert ctypes.sizeof(B.Diag) == 16
 
@@ -60,6 +60,8 @@ def _dims(lib, **kw):
     (dict(d_ff=96), B.MOE_ERR_UNSUPPORTED),
     (dict(d_ff_shared=32), B.MOE_ERR_UNSUPPORTED),
     (dict(d_ff_shared=-64), B.MOE_ERR_INVALID_VALUE),
+    (dict(n_routed=0, top_k=0, d_ff_shared=0), B.MOE_ERR_INVALID_VALUE),  # a dense layer needs its MLP
+    (dict(capacity=-1), B.MOE_ERR_INVALID_VALUE),
 ])
 def test_bad_dims(lib, kw, status):
     with pytest.raises(fgr.MoeError) as ei:
@@ -159,3 +161,51 @@ def test_prefill_operand_limit_is_checked_before_any_launch(lib):
         lib.expert_ffn(d, T, FAKE, _full_weights(lib), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_bytes=need,
                        stream=0)
     assert ei.value.status == B.MOE_ERR_UNSUPPORTED
+
+
+def test_dense_layer_dims_are_valid_and_routing_calls_refuse_them(lib):
+    d = _dims(lib, n_routed=0, top_k=0, d_ff=0, d_ff_shared=640)
+    need = lib.workspace_size(d, 100)
+    assert need > 0
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.router_topk(d, 4, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws_bytes=need, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE and "routed" in str(ei.value)
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.permute(d, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes=need, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE
+    with pytest.raises(fgr.MoeError) as ei:  # the dense MLP's weights are required
+        lib.layer_forward(d, 4, FAKE, lib.weights(), FAKE, None, FAKE, ws_bytes=need, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE and "w1s" in str(ei.value)
+    with pytest.raises(fgr.MoeError) as ei:  # combine of a dense layer needs y_shared
+        lib.combine(d, 4, None, None, None, None, FAKE, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE and "y_shared" in str(ei.value)
+
+
+def test_capacity_seats_exact():
+    assert fgr.capacity_seats(1.0, 16384, 8, 256) == 512
+    assert fgr.capacity_seats(1.1, 16384, 8, 256) == 564
+    assert fgr.capacity_seats(0.5, 3, 2, 3) == 1
+
+
+def test_rmsnorm_and_block_validation(lib):
+    d = _dims(lib)
+    lib.rmsnorm(d, 0, None, None, 1e-6, None, stream=0)  # T = 0: no-op
+    lib.block_forward(d, 0, None, None, 1e-6, lib.weights(), None, None, None, ws_bytes=0, stream=0)
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.rmsnorm(d, 4, FAKE, None, 1e-6, FAKE * 2, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE and "norm_weight" in str(ei.value)
+    for eps in (-1.0, float("nan"), float("inf")):
+        with pytest.raises(fgr.MoeError) as ei:
+            lib.rmsnorm(d, 4, FAKE, FAKE, eps, FAKE * 2, stream=0)
+        assert ei.value.status == B.MOE_ERR_INVALID_VALUE and "eps" in str(ei.value)
+    with pytest.raises(fgr.MoeError) as ei:  # u overlaps x
+        lib.rmsnorm(d, 4, FAKE, FAKE, 1e-6, FAKE + 256, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE and "overlaps" in str(ei.value)
+    need = lib.workspace_size(d, 4)
+    with pytest.raises(fgr.MoeError) as ei:  # out aliases x
+        lib.block_forward(d, 4, FAKE, FAKE, 1e-6, _full_weights(lib), FAKE, None, FAKE * 2, ws_bytes=need, stream=0)
+    assert ei.value.status == B.MOE_ERR_INVALID_VALUE and "overlaps" in str(ei.value)
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.block_forward(d, 4, FAKE, FAKE, 1e-6, _full_weights(lib), FAKE * 2, None, FAKE * 4, ws_bytes=need - 1,
+                          stream=0)
+    assert ei.value.status == B.MOE_ERR_WORKSPACE

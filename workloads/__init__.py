@@ -53,6 +53,8 @@ __all__ = [
     "ROW_BLOCK",
     "F64Experts",
     "make_block_inputs",
+    "make_x",
+    "make_gamma",
     "NORM_EPS",
 ]
 
@@ -211,12 +213,17 @@ def make_x(wl: Workload, seed: int = 0, device="cpu", T: Optional[int] = None) -
     return out
 
 
+def make_gamma(wl: Workload, seed: int = 0, device="cpu") -> torch.Tensor:
+    """RMSNorm gain [d] fp32."""
+    return 1.0 + 0.1 * _randn((wl.d,), _seed(seed, wl.family, "gamma", 0), device)
+
+
 def make_block_inputs(wl: Workload, seed: int = 0, device="cpu", T: Optional[int] = None):
     """Inputs of one pre-norm block: the weights, the raw stream ``x`` and the
     RMSNorm gain ``gamma`` [d] fp32 (no ``u``: the block computes it)."""
     inp = make_weights(wl, seed, device)
     inp["x"] = make_x(wl, seed, device, T)
-    inp["gamma"] = 1.0 + 0.1 * _randn((wl.d,), _seed(seed, wl.family, "gamma", 0), device)
+    inp["gamma"] = make_gamma(wl, seed, device)
     return inp
 
 
