@@ -8,6 +8,12 @@ stream; the roofline block reports the dominant kernel (grouped gate/up GEMM)
 against the bf16 dense matrix-core peak.  A decode-size measurement (T = 64,
 same weights) reports achieved HBM bandwidth over the touched experts'
 weights.  The CPU oracle is timed on a bounded token slice as a baseline.
+
+Other lines (one JSON line each, same fields):
+  --workload dsv3_dense_prefill   the dense prefix layer FFN (width 18432), and
+                                  its T = 64 decode size;
+  --block                         the pre-norm block x + layer(RMSNorm(x));
+  --capacity-factor CF            the layer with ceil(CF * T * k / N_r) seats per expert.
 """
 import argparse
 import ctypes
@@ -72,30 +78,30 @@ class HipEvents:
         return out.value
 
 
-def timed_steps(layer, u, steps, warmup, path, hev):
+def timed_steps(step, steps, warmup, hev, stages=STAGES):
+    """Time `steps` calls of step(events) after `warmup` untimed ones; the library
+    records len(stages) + 1 events per call at its stage boundaries."""
     import torch
     for _ in range(warmup):
-        layer.forward(u, path=path)
-    evs = [hev.create(7) for _ in range(steps)]
+        step(None)
+    evs = [hev.create(len(stages) + 1) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
-        layer.forward(u, path=path, events=evs[s])
+        step(evs[s])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    stage = {name: sum(hev.ms(e[i], e[i + 1]) for e in evs) / steps for i, name in enumerate(STAGES)}
-    total = sum(hev.ms(e[0], e[6]) for e in evs) / steps
+    stage = {name: sum(hev.ms(e[i], e[i + 1]) for e in evs) / steps for i, name in enumerate(stages)}
+    total = sum(hev.ms(e[0], e[len(stages)]) for e in evs) / steps
     return wall_ms, total, stage
 
 
-def cpu_baseline(wl, inp, n_tokens):
+def cpu_baseline(wl, inp, n_tokens, block=False):
     """The oracle as it stands, on the first n_tokens tokens (weights staged on the host, untimed)."""
     import torch
-    import numpy as np
     import oracle
     import workloads
     host = {k: (None if v is None else v.to("cpu")) for k, v in inp.items()}
-    u64 = host["u"][:n_tokens].to(torch.float64).numpy()
     args = dict(w_router=workloads.to_f64(host["w_router"]), w1=workloads.F64Experts(host["w1"]),
                 w3=workloads.F64Experts(host["w3"]), w2=workloads.F64Experts(host["w2"]), k=wl.top_k,
                 bias=workloads.to_f64(host["router_bias"]), w1s=workloads.to_f64(host["w1s"]),
@@ -106,12 +112,21 @@ def cpu_baseline(wl, inp, n_tokens):
     except Exception:
         blas = 1
     cores = max(blas, torch.get_num_threads())
+    what = "fp64 numpy oracle incl. per-expert widening of host bf16 weights to fp64"
     t0 = time.perf_counter()
-    oracle.forward(u64, **args)
+    if block:
+        x64 = host["x"][:n_tokens].to(torch.float64).numpy()
+        g64 = host["gamma"].to(torch.float64).numpy()
+        oracle.block_forward(x64, g64, workloads.NORM_EPS, wl.dtype, **args)
+        what = "fp64 numpy oracle of the pre-norm block (RMSNorm, layer, residual)"
+    elif wl.top_k == 0:
+        oracle.dense_ffn(host["u"][:n_tokens].to(torch.float64).numpy(), args["w1s"], args["w3s"], args["w2s"])
+        what = "fp64 numpy oracle of the dense SwiGLU"
+    else:
+        oracle.forward(host["u"][:n_tokens].to(torch.float64).numpy(), **args)
     dt = time.perf_counter() - t0
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n_tokens} tokens of {wl.name}; fp64 numpy oracle incl. per-expert widening of "
-                      f"host bf16 weights to fp64; {dt:.1f} s"}
+            "sample": f"first {n_tokens} tokens of {wl.name}; {what}; {dt:.1f} s"}
 
 
 def main():
@@ -120,8 +135,12 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dsv3_prefill")
+    ap.add_argument("--block", action="store_true", help="time the pre-norm block instead of the bare layer")
+    ap.add_argument("--capacity-factor", type=float, default=0.0,
+                    help="seat limit ceil(CF * T * k / N_r) per expert (0: no limit)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens the oracle baseline runs on (default: 64 for the MoE layer, 16384 dense)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -134,7 +153,7 @@ def main():
 
     import torch
     import workloads
-    from fine_grained_routed_amd import PATH_AUTO, PATH_DECODE, MoELayer
+    from fine_grained_routed_amd import PATH_AUTO, PATH_DECODE, MoELayer, capacity_seats
 
     torch.cuda.set_device(0)
     if args.calibrate_copy:
@@ -147,22 +166,48 @@ def main():
         print(json.dumps({"copy_bytes_per_dispatch": n * 4, "dispatches": 3}), flush=True)
         return
     wl = workloads.get(args.workload)
+    dense = wl.top_k == 0
     print(f"[bench] drawing inputs for {wl.name}", file=sys.stderr, flush=True)
-    inp = workloads.make_inputs(wl, seed=args.seed, device="cuda")
-    layer = MoELayer({k: v for k, v in inp.items() if k != "u"}, wl.top_k)
+    inp = (workloads.make_block_inputs if args.block else workloads.make_inputs)(wl, seed=args.seed, device="cuda")
+    cap = capacity_seats(args.capacity_factor, wl.T, wl.top_k, wl.n_routed) if args.capacity_factor > 0 else 0
+    weights = {k: v for k, v in inp.items() if k not in ("u", "x", "gamma")}
+    layer = MoELayer(weights, wl.top_k, capacity=cap)
     hev = HipEvents()
-    u = inp["u"]
-    T = u.shape[0]
+    if args.block:
+        x, gamma = inp["x"], inp["gamma"]
+        T = x.shape[0]
+        stages = ["rmsnorm"] + STAGES
+        step = lambda ev: layer.block_forward(x, gamma, workloads.NORM_EPS, path=PATH_AUTO, events=ev)
+    else:
+        u = inp["u"]
+        T = u.shape[0]
+        stages = STAGES
+        step = lambda ev: layer.forward(u, path=PATH_AUTO, events=ev)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    wall_ms, ev_ms, stage = timed_steps(layer, u, args.steps, args.warmup, PATH_AUTO, hev)
+    wall_ms, ev_ms, stage = timed_steps(step, args.steps, args.warmup, hev, stages)
 
     R = T * wl.top_k
     gu_flop = 4.0 * wl.d * (R * wl.d_ff + T * wl.d_ff_shared)
     dn_flop = gu_flop / 2.0
     total_flop = wl.flops(T)
     gu_tflops = gu_flop / (stage["gate_up"] * 1e-3) / 1e12
+    if dense:
+        metric = "dense prefix FFN tokens/s at DeepSeek-V3 shape (d=7168, width 18432); % bf16 MFMA peak"
+    elif args.block:
+        metric = "pre-norm MoE block tokens/s at DeepSeek-V3 shape (RMSNorm + layer + residual)"
+    else:
+        metric = "MoE-layer tokens/s at DeepSeek-V3 shape; % bf16 MFMA peak (prefill), % HBM (decode)"
+    config = {"workload": wl.name, "T": T, "d_model": wl.d, "n_routed": wl.n_routed, "d_ff": wl.d_ff,
+              "n_shared": wl.n_shared, "top_k": wl.top_k}
+    if dense:
+        config = {"workload": wl.name, "T": T, "d_model": wl.d, "width": wl.d_ff_shared}
+    if args.block:
+        config["block"] = "x + layer(RMSNorm(x))"
+    if cap:
+        config["capacity_factor"] = args.capacity_factor
+        config["capacity_seats"] = cap
     result = {
-        "metric": "MoE-layer tokens/s at DeepSeek-V3 shape; % bf16 MFMA peak (prefill), % HBM (decode)",
+        "metric": metric,
         "value": T / (wall_ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -173,13 +218,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic: seeded RMS-normalised N(0,1) tokens, N(0,0.02) weights",
-        "config": {"workload": wl.name, "T": T, "d_model": wl.d, "n_routed": wl.n_routed, "d_ff": wl.d_ff,
-                   "n_shared": wl.n_shared, "top_k": wl.top_k},
+        "data": "synthetic: seeded RMS-normalised N(0,1) tokens, N(0,0.02) weights"
+                + ("; block input: per-token scaled N(0,1) stream, gain 1+N(0,0.1)" if args.block else ""),
+        "config": config,
         "roofline": {"bound": "mfma", "kernel": "grouped_gemm_bf16_kernel<gate_up>",
                      "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": gu_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": measured_traffic("gate_up_prefill", "ffn_prefill.hip"),
+                     "traffic": measured_traffic("dense_gate_up_prefill" if dense else "gate_up_prefill",
+                                                 "ffn_prefill.hip") if not (args.block or cap) else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         "layer_tflops": total_flop / (wall_ms * 1e-3) / 1e12,
         "layer_frac_of_peak": total_flop / (wall_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -187,14 +233,29 @@ def main():
         "event_ms_per_step": ev_ms,
         "down_tflops": dn_flop / (stage["down"] * 1e-3) / 1e12,
     }
+    if args.block:
+        eb = 2 if wl.dtype == "bf16" else 4
+        nb = 2 * T * wl.d * eb + 4 * wl.d  # read x, write u, read the gain
+        result["rmsnorm"] = {"bound": "hbm", "bytes": nb, "achieved": nb / (stage["rmsnorm"] * 1e-3) / 1e9,
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": nb / (stage["rmsnorm"] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    if cap:
+        idx, _ = layer.router_topk(inp["u"])
+        kept = int(layer.permute(idx)[1][-1].item())
+        result["capacity_dropped_pairs"] = R - kept
 
-    if not args.no_decode and wl.name == "dsv3_prefill":
-        dec = workloads.get("dsv3_decode")
-        ud = u[:dec.T].contiguous()
-        d_wall, d_ev, d_stage = timed_steps(layer, ud, max(args.steps, 20), args.warmup, PATH_DECODE, hev)
-        idx, _ = layer.router_topk(ud)
-        counts = layer.permute(idx)[0].cpu()
-        touched = int((counts > 0).sum())
+    dec_name = {"dsv3_prefill": "dsv3_decode", "dsv3_dense_prefill": "dsv3_dense_decode"}.get(wl.name)
+    if not args.no_decode and not args.block and not cap and dec_name:
+        dec = workloads.get(dec_name)
+        ud = inp["u"][:dec.T].contiguous()
+        d_wall, d_ev, d_stage = timed_steps(lambda ev: layer.forward(ud, path=PATH_DECODE, events=ev),
+                                            max(args.steps, 20), args.warmup, hev)
+        if dense:
+            touched = 0
+        else:
+            idx, _ = layer.router_topk(ud)
+            counts = layer.permute(idx)[0].cpu()
+            touched = int((counts > 0).sum())
         eb = 2  # bf16
         gu_bytes = eb * (touched * 2 * wl.d_ff * wl.d + 2 * wl.d_ff_shared * wl.d)
         dn_bytes = eb * (touched * wl.d * wl.d_ff + wl.d * wl.d_ff_shared)
@@ -207,13 +268,15 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "gate_up (decode path)",
                          "achieved": gu_bytes / (d_stage["gate_up"] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": gu_bytes / (d_stage["gate_up"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "traffic": measured_traffic("gate_up_decode", "ffn_decode.hip"),
+                         "traffic": measured_traffic("dense_gate_up_decode" if dense else "gate_up_decode",
+                                                     "ffn_decode.hip"),
                          "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         }
 
     if not args.no_cpu_baseline:
-        print(f"[bench] timing the oracle on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_tokens)
+        n_cpu = args.cpu_tokens or (16384 if dense else 64)
+        print(f"[bench] timing the oracle on {n_cpu} tokens", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, inp, n_cpu, block=args.block)
     print(json.dumps(result), flush=True)
 
 

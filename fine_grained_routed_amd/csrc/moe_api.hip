@@ -128,7 +128,7 @@ static moe_status check_opts(const moe_options *o) {
 static int pick_path(const moe_dims &dm, int64_t T, const moe_options *o) {
   const int want = o ? o->path : 0;
   if (want != 0) return want;
-  if (dm.n_routed == 0) return T <= 64 ? 2 : 1;
+  if (dm.n_routed == 0) return T <= 32 ? 2 : 1;
   return (T * dm.top_k <= 2 * (int64_t)dm.n_routed && T <= 256) ? 2 : 1;
 }
 
@@ -386,6 +386,7 @@ moe_status moe_block_forward(const moe_dims *dims, int64_t T, const void *x, con
   EventHook ev{opts, st};
   ev.rec(0);
   MOE_TRY_HIP(launch_rmsnorm(*dims, T, x, norm_weight, eps, u, st), "rmsnorm");
+  ev.rec(1);
   ev.base = 1;
   return run_layer(*dims, T, u, *wts, x, out, opts, L, w, st, ev);
 }

@@ -56,6 +56,7 @@ DENSE = [
     ("dense_small", None, PATH_PREFILL),
     ("dense_small", None, PATH_DECODE),
     ("dense_small", 1, PATH_AUTO),
+    ("dense_small", 32, PATH_AUTO),
     ("dense_small", 63, PATH_AUTO),
     ("dense_small", 257, PATH_PREFILL),
     ("dense_small_f32", None, PATH_AUTO),
