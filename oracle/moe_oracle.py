@@ -109,7 +109,30 @@ def softmax(l) -> np.ndarray:
     return z / z.sum(axis=-1, keepdims=True)
 
 
-def route(u, w_router, k: int, bias=None):
+def _kept_groups(l_t, lo_t, hi_t, n_group: int, topk_group: int, exact_of):
+    """The topk_group groups with the largest best-expert logit (ties to the lower
+    group index), as a sorted list.  Experts are split into n_group contiguous
+    groups of N_r / n_group.  Returns (groups, settled_exactly)."""
+    G = l_t.shape[0] // n_group
+    gl, glo, ghi = (a.reshape(n_group, G).max(axis=1) for a in (l_t, lo_t, hi_t))
+    order = np.lexsort((np.arange(n_group), -gl))
+    kept = order[:topk_group]
+    if topk_group == n_group or glo[kept].min() > ghi[order[topk_group:]].max():
+        return sorted(int(g) for g in kept), False
+    # A group whose upper bound is below the topk_group-th largest lower bound has
+    # that many groups certainly above it; inside a group, only experts whose upper
+    # bound reaches the group's largest lower bound can be its best expert.
+    cut = np.sort(glo)[::-1][topk_group - 1]
+    best = {}
+    for g in range(n_group):
+        if ghi[g] >= cut:
+            es = [g * G + i for i in range(G) if hi_t[g * G + i] >= glo[g]]
+            best[g] = max(exact_of(e) for e in es)
+    ranked = sorted(best, key=lambda g: (-best[g], g))
+    return sorted(ranked[:topk_group]), True
+
+
+def route(u, w_router, k: int, bias=None, n_group: Optional[int] = None, topk_group: Optional[int] = None):
     """Per-token top-k selection and gates.
 
     Returns (topk_idx [T,k] int32, topk_w [T,k] fp64, logits [T,N_r] fp64,
@@ -121,32 +144,56 @@ def route(u, w_router, k: int, bias=None):
     every comparison that decides the ordered top-k is separated by more than
     the two error bounds; otherwise the candidates that may belong to the
     top-k are re-ranked by their exact rational logits.
+
+    Group-limited routing (n_group, topk_group): "Shared and fine-grained
+    experts" names DeepSeek-V3's node-limited routing (Developer level, 'Why not
+    go finer still': it caps the machines a token's experts live on; Researcher
+    level, Systems limits: n_group 8, topk_group 4); the rule for scoring a
+    group is not on the pages.  Reading: the
+    experts form n_group contiguous groups, a group's score is its best expert's
+    logit, the token keeps the topk_group best groups (ties to the lower group
+    index) and its top-k is taken among their experts only.  The gates stay the
+    full-softmax probabilities.
     """
     u = _f64(u)
     w = _f64(w_router)
     T, E = u.shape[0], w.shape[0]
     if not (1 <= k <= E):
         raise ValueError("top_k must be in [1, n_routed]")
+    grouped = n_group is not None and n_group > 1 and topk_group is not None and topk_group < n_group
+    if grouped and (E % n_group or not 1 <= topk_group or topk_group * (E // n_group) < k):
+        raise ValueError("need N_r divisible by n_group and topk_group * N_r / n_group >= k")
     l, beta = router_logits(u, w, bias)
     lo, hi = l - beta, l + beta
     idx = np.empty((T, k), dtype=np.int32)
     n_exact = 0
     experts = np.arange(E)
+    b = None if bias is None else _f64(bias)
     for t in range(T):
-        order = np.lexsort((experts, -l[t]))  # descending logit, ties -> lower index
+        exact_of = lambda e: exact_logit(u[t], w[e], None if b is None else b[e])
+        lt, lot, hit = l[t], lo[t], hi[t]
+        settled_exactly = False
+        if grouped:
+            kept, settled_exactly = _kept_groups(lt, lot, hit, n_group, topk_group, exact_of)
+            out = np.ones(E, dtype=bool)
+            G = E // n_group
+            for g in kept:
+                out[g * G:(g + 1) * G] = False
+            lt, lot, hit = (np.where(out, -np.inf, a) for a in (lt, lot, hit))
+        order = np.lexsort((experts, -lt))  # descending logit, ties -> lower index
         top = order[:k]
-        ok = all(lo[t, top[j]] > hi[t, top[j + 1]] for j in range(k - 1))
+        ok = all(lot[top[j]] > hit[top[j + 1]] for j in range(k - 1))
         if ok and k < E:
-            ok = lo[t, top[k - 1]] > hi[t, order[k:]].max()
+            ok = lot[top[k - 1]] > hit[order[k:]].max()
         if not ok:
-            n_exact += 1
+            settled_exactly = True
             # Any expert whose upper bound is below the k-th largest lower bound
             # has at least k experts certainly above it: it cannot be selected.
-            kth_lo = np.sort(lo[t])[::-1][k - 1]
-            cand = [int(e) for e in experts if hi[t, e] >= kth_lo]
-            b = None if bias is None else _f64(bias)
-            keys = {e: exact_logit(u[t], w[e], None if b is None else b[e]) for e in cand}
+            kth_lo = np.sort(lot)[::-1][k - 1]
+            cand = [int(e) for e in experts if hit[e] >= kth_lo]
+            keys = {e: exact_of(e) for e in cand}
             top = sorted(cand, key=lambda e: (-keys[e], e))[:k]
+        n_exact += settled_exactly
         idx[t] = top
     p = softmax(l)
     gates = np.take_along_axis(p, idx.astype(np.int64), axis=1)
@@ -260,11 +307,12 @@ def combine(y_rows, y_shared, topk_w, token_row):
 
 
 def forward(u, w_router, w1, w3, w2, k: int, bias=None, w1s=None, w3s=None, w2s=None,
-            capacity: Optional[int] = None):
+            capacity: Optional[int] = None, n_group: Optional[int] = None, topk_group: Optional[int] = None):
     """The whole layer: route, group, run experts, combine.  Returns a dict.
-    capacity: seats per expert (see ``permute``); None = no limit."""
+    capacity: seats per expert (see ``permute``); None = no limit.
+    n_group, topk_group: group-limited routing (see ``route``); None = none."""
     E = _f64(w_router).shape[0]
-    idx, gates, l, n_exact = route(u, w_router, k, bias)
+    idx, gates, l, n_exact = route(u, w_router, k, bias, n_group, topk_group)
     counts, offsets, row_token, token_row = permute(idx, E, capacity)
     y_rows, y_shared = expert_ffn(u, w1, w3, w2, counts, offsets, row_token, w1s, w3s, w2s)
     out = combine(y_rows, y_shared, gates, token_row)

@@ -11,6 +11,7 @@ import oracle
 import oracle.block as ob
 import oracle.moe_oracle as om
 from tests import test_oracle_block as B
+from tests import test_oracle_groups as GR
 from tests import test_oracle_layer as L
 from tests import test_oracle_router as R
 
@@ -141,8 +142,27 @@ def _combine_wraps_dropped(y_rows, y_shared, topk_w, token_row):
     return out
 
 
+def _groups_by_sum(l_t, lo_t, hi_t, n_group, topk_group, exact_of):
+    gs = l_t.reshape(n_group, -1).sum(axis=1)
+    return sorted(int(g) for g in np.lexsort((np.arange(n_group), -gs))[:topk_group]), False
+
+
+def _groups_ties_high(l_t, lo_t, hi_t, n_group, topk_group, exact_of):
+    gl = l_t.reshape(n_group, -1).max(axis=1)
+    return sorted(int(g) for g in np.lexsort((-np.arange(n_group), -gl))[:topk_group]), False
+
+
+def _groups_fp64_only(l_t, lo_t, hi_t, n_group, topk_group, exact_of):
+    gl = l_t.reshape(n_group, -1).max(axis=1)
+    return sorted(int(g) for g in np.lexsort((np.arange(n_group), -gl))[:topk_group]), False
+
+
+def _groups_ignored(l_t, lo_t, hi_t, n_group, topk_group, exact_of):
+    return list(range(n_group)), False
+
+
 _orig = {n: getattr(om, n) for n in ("silu", "swiglu", "combine", "route", "permute", "router_logits",
-                                     "capacity_seats")}
+                                     "capacity_seats", "_kept_groups")}
 _orig_b = {n: getattr(ob, n) for n in ("round_to_bf16", "rms_norm", "block_forward")}
 
 MUTANTS = [
@@ -162,6 +182,10 @@ MUTANTS = [
     ("capacity_seats", _seats_floor, [lambda: B.test_capacity_seats_hand_values(1.1, 16384, 8, 256, 564)]),
     ("combine", _combine_wraps_dropped, [B.test_capacity_drops_contribute_nothing,
                                          B.test_capacity_zero_leaves_exactly_the_shared_output]),
+    ("_kept_groups", _groups_by_sum, [GR.test_group_score_is_the_best_expert_not_the_sum]),
+    ("_kept_groups", _groups_ties_high, [GR.test_equal_group_scores_go_to_the_lower_group]),
+    ("_kept_groups", _groups_fp64_only, [GR.test_group_scores_a_sub_ulp_apart_are_decided_exactly]),
+    ("_kept_groups", _groups_ignored, [GR.test_group_limit_changes_the_choice_hand_example]),
 ]
 
 MUTANTS_BLOCK = [
@@ -179,7 +203,8 @@ MUTANTS_BLOCK = [
 @pytest.mark.parametrize("name,mutant,pins", MUTANTS, ids=[f"{m[0]}:{m[1].__name__}" for m in MUTANTS])
 def test_pins_catch_planted_mistake(monkeypatch, name, mutant, pins):
     monkeypatch.setattr(om, name, mutant)
-    monkeypatch.setattr(oracle, name, mutant)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, mutant)
     caught = 0
     for pin in pins:
         try:
