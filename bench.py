@@ -13,7 +13,8 @@ Other lines (one JSON line each, same fields):
   --workload dsv3_dense_prefill   the dense prefix layer FFN (width 18432), and
                                   its T = 64 decode size;
   --block                         the pre-norm block x + layer(RMSNorm(x));
-  --capacity-factor CF            the layer with ceil(CF * T * k / N_r) seats per expert.
+  --capacity-factor CF            the layer with ceil(CF * T * k / N_r) seats per expert;
+  --groups NG,TG                  the layer with group-limited top-k (NG groups, TG kept).
 """
 import argparse
 import ctypes
@@ -138,6 +139,8 @@ def main():
     ap.add_argument("--block", action="store_true", help="time the pre-norm block instead of the bare layer")
     ap.add_argument("--capacity-factor", type=float, default=0.0,
                     help="seat limit ceil(CF * T * k / N_r) per expert (0: no limit)")
+    ap.add_argument("--groups", default="", metavar="NG,TG",
+                    help="group-limited routing: NG expert groups, TG kept per token (e.g. 8,4)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens the oracle baseline runs on (default: 64 for the MoE layer, 16384 dense)")
@@ -171,7 +174,8 @@ def main():
     inp = (workloads.make_block_inputs if args.block else workloads.make_inputs)(wl, seed=args.seed, device="cuda")
     cap = capacity_seats(args.capacity_factor, wl.T, wl.top_k, wl.n_routed) if args.capacity_factor > 0 else 0
     weights = {k: v for k, v in inp.items() if k not in ("u", "x", "gamma")}
-    layer = MoELayer(weights, wl.top_k, capacity=cap)
+    ng, tg = (int(v) for v in args.groups.split(",")) if args.groups else (0, 0)
+    layer = MoELayer(weights, wl.top_k, capacity=cap, n_group=ng, topk_group=tg)
     hev = HipEvents()
     if args.block:
         x, gamma = inp["x"], inp["gamma"]
@@ -195,6 +199,8 @@ def main():
         metric = "dense prefix FFN tokens/s at DeepSeek-V3 shape (d=7168, width 18432); % bf16 MFMA peak"
     elif args.block:
         metric = "pre-norm MoE block tokens/s at DeepSeek-V3 shape (RMSNorm + layer + residual)"
+    elif ng:
+        metric = "MoE-layer tokens/s at DeepSeek-V3 shape with group-limited top-k"
     else:
         metric = "MoE-layer tokens/s at DeepSeek-V3 shape; % bf16 MFMA peak (prefill), % HBM (decode)"
     config = {"workload": wl.name, "T": T, "d_model": wl.d, "n_routed": wl.n_routed, "d_ff": wl.d_ff,
@@ -206,6 +212,8 @@ def main():
     if cap:
         config["capacity_factor"] = args.capacity_factor
         config["capacity_seats"] = cap
+    if ng:
+        config["n_group"], config["topk_group"] = ng, tg
     result = {
         "metric": metric,
         "value": T / (wall_ms * 1e-3),
@@ -225,7 +233,7 @@ def main():
                      "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": gu_tflops / PEAK_BF16_TFLOPS,
                      "traffic": measured_traffic("dense_gate_up_prefill" if dense else "gate_up_prefill",
-                                                 "ffn_prefill.hip") if not (args.block or cap) else None,
+                                                 "ffn_prefill.hip") if not (args.block or cap or ng) else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         "layer_tflops": total_flop / (wall_ms * 1e-3) / 1e12,
         "layer_frac_of_peak": total_flop / (wall_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -245,7 +253,7 @@ def main():
         result["capacity_dropped_pairs"] = R - kept
 
     dec_name = {"dsv3_prefill": "dsv3_decode", "dsv3_dense_prefill": "dsv3_dense_decode"}.get(wl.name)
-    if not args.no_decode and not args.block and not cap and dec_name:
+    if not args.no_decode and not args.block and not cap and not ng and dec_name:
         dec = workloads.get(dec_name)
         ud = inp["u"][:dec.T].contiguous()
         d_wall, d_ev, d_stage = timed_steps(lambda ev: layer.forward(ud, path=PATH_DECODE, events=ev),

@@ -33,7 +33,8 @@ class MoeError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("n_routed", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("d_ff_shared", ctypes.c_int32), ("top_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("capacity", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("capacity", ctypes.c_int32), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -112,8 +113,9 @@ class Library:
             raise MoeError(status, self.last_error())
 
     @staticmethod
-    def dims(d_model, n_routed, d_ff, d_ff_shared, top_k, dtype=MOE_BF16, out_dtype=MOE_F32, capacity=0) -> Dims:
-        return Dims(d_model, n_routed, d_ff, d_ff_shared, top_k, dtype, out_dtype, capacity)
+    def dims(d_model, n_routed, d_ff, d_ff_shared, top_k, dtype=MOE_BF16, out_dtype=MOE_F32, capacity=0,
+             n_group=0, topk_group=0) -> Dims:
+        return Dims(d_model, n_routed, d_ff, d_ff_shared, top_k, dtype, out_dtype, capacity, n_group, topk_group)
 
     @staticmethod
     def weights(w_router=None, router_bias=None, w1=None, w3=None, w2=None, w1s=None, w3s=None, w2s=None) -> Weights:

@@ -52,6 +52,15 @@ static moe_status check_dims(const moe_dims *dm, int64_t T) {
   }
   if (dm->d_model < 1 || dm->d_ff < 0 || dm->d_ff_shared < 0) return fail(MOE_ERR_INVALID_VALUE, "non-positive width");
   if (dm->capacity < 0) return fail(MOE_ERR_INVALID_VALUE, "capacity < 0");
+  if (dm->n_group < 0) return fail(MOE_ERR_INVALID_VALUE, "n_group < 0");
+  if (dm->n_group > 1 && !dense) {
+    if (dm->n_group > 64) return fail(MOE_ERR_UNSUPPORTED, "n_group > 64");
+    if (dm->n_routed % dm->n_group) return fail(MOE_ERR_INVALID_VALUE, "n_routed is not a multiple of n_group");
+    if (dm->topk_group < 1 || dm->topk_group > dm->n_group)
+      return fail(MOE_ERR_INVALID_VALUE, "topk_group must be in [1, n_group]");
+    if ((int64_t)dm->topk_group * (dm->n_routed / dm->n_group) < dm->top_k)
+      return fail(MOE_ERR_INVALID_VALUE, "topk_group groups hold fewer than top_k experts");
+  }
   if (dm->dtype != MOE_F32 && dm->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dm->dtype);
   if (dm->out_dtype != MOE_F32 && dm->out_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "unknown out_dtype %d", dm->out_dtype);

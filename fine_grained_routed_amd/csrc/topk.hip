@@ -19,6 +19,16 @@
 // are exact in fp64) and the largest wins, ties to the lower index.  A product
 // that falls below the fixed-point window (a dynamic range above ~2^200 inside
 // one token) raises a diagnostics flag instead of being dropped silently.
+//
+// Group-limited routing ("Shared and fine-grained experts": node-limited
+// routing caps the machines a token's experts live on, DeepSeek-V3's n_group 8
+// and topk_group 4).  Read as: experts form contiguous groups of G, a group
+// scores its best expert, the token keeps its topk_group best groups (ties to
+// the lower group) and takes its top-k among their experts.  The rounds above
+// walk the experts in exact descending key order, so the first topk_group
+// groups that walk meets are exactly the kept groups: from the round that
+// meets the last of them on, every other group's experts leave the candidate
+// set, and every winner is a kept expert.
 #include "common.h"
 
 double router_bound_coeff(const moe_dims &dm);
@@ -151,9 +161,9 @@ template <int S, bool BF16>
 __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ logits, const double *__restrict__ un2,
                                                    const double *__restrict__ wn2, const float *__restrict__ bias,
                                                    const void *__restrict__ u, const void *__restrict__ w,
-                                                   int64_t T, int E, int d, int k, double c1,
-                                                   int32_t *__restrict__ idx_out, float *__restrict__ w_out,
-                                                   DiagWords *diag) {
+                                                   int64_t T, int E, int d, int k, double c1, int G,
+                                                   int topk_group, int32_t *__restrict__ idx_out,
+                                                   float *__restrict__ w_out, DiagWords *diag) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * TOPK_TOKENS_PER_WG + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -190,6 +200,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
   int eu = -100000;  // max exponent of |u_t,i|, computed on first need
   const double c64 = (d / 64 + 8) * 0x1p-52;  // fp64 refinement bound coefficient
   unsigned refined = 0;                         // slots whose L/B hold fp64 values
+  unsigned long long kept = 0;                  // groups met so far (G > 0)
+  int nkept = 0;
   for (int j = 0; j < k; ++j) {
     int win = -1;
     for (;;) {
@@ -275,6 +287,19 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
       if (lane == 0) atomicAdd(&diag->exact_keys, (unsigned)cnt);
       break;
     }
+    if (G > 0) {  // group-limited: the winner's group is kept (it is one of the first topk_group met)
+      const int g = win / G;
+      if (!((kept >> g) & 1ull)) {
+        kept |= 1ull << g;
+        if (++nkept == topk_group) {
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            const int e = lane + 64 * s;
+            if (e < E && !((kept >> (e / G)) & 1ull)) avail &= ~(1u << s);
+          }
+        }
+      }
+    }
     // take the winner out and emit its slot
     double lw = NEG;
 #pragma unroll
@@ -305,12 +330,15 @@ static void launch_topk_s(const moe_dims &dm, int64_t T, const void *u, const vo
   const double *un2 = (const double *)(ws + L.unorm2);
   const double *wn2 = (const double *)(ws + L.wnorm2);
   DiagWords *diag = (DiagWords *)(ws + L.diag);
+  // group size, or 0 when routing is not group-limited
+  const bool grouped = dm.n_group > 1 && dm.topk_group < dm.n_group;
+  const int G = grouped ? dm.n_routed / dm.n_group : 0;
   if (dm.dtype == MOE_BF16)
     topk_kernel<S, true><<<grid, 256, 0, st>>>(lg, un2, wn2, bias, u, w, T, dm.n_routed, dm.d_model, dm.top_k, c1,
-                                               idx, wout, diag);
+                                               G, dm.topk_group, idx, wout, diag);
   else
     topk_kernel<S, false><<<grid, 256, 0, st>>>(lg, un2, wn2, bias, u, w, T, dm.n_routed, dm.d_model, dm.top_k, c1,
-                                                idx, wout, diag);
+                                                G, dm.topk_group, idx, wout, diag);
 }
 
 hipError_t launch_topk(const moe_dims &dm, int64_t T, const void *u, const void *w_router, const float *bias,

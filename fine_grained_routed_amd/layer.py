@@ -18,10 +18,11 @@ class MoELayer:
     optional w1s/w3s [f_s,d], w2s [d,f_s] and router_bias [N_r] fp32.  A dense
     layer has top_k == 0 and no routed experts (w_router None or with 0 rows);
     its MLP is w1s/w3s/w2s.  capacity: seats per routed expert (0 = no limit).
+    n_group, topk_group: group-limited routing (n_group <= 1: none).
     """
 
     def __init__(self, weights: Dict[str, Optional[torch.Tensor]], top_k: int, out_dtype=torch.float32,
-                 lib: Optional[Library] = None, capacity: int = 0):
+                 lib: Optional[Library] = None, capacity: int = 0, n_group: int = 0, topk_group: int = 0):
         self.lib = lib or load()
         self.w = weights
         for name, t in weights.items():
@@ -37,7 +38,9 @@ class MoELayer:
         self.dtype = ref.dtype
         self.out_dtype = out_dtype
         self.capacity = capacity
-        self.dims = self.lib.dims(self.d, self.E, self.f, self.fs, top_k, _DT[ref.dtype], _DT[out_dtype], capacity)
+        self.n_group, self.topk_group = n_group, topk_group
+        self.dims = self.lib.dims(self.d, self.E, self.f, self.fs, top_k, _DT[ref.dtype], _DT[out_dtype], capacity,
+                                  n_group, topk_group)
         routed = self.E > 0
         self.cw = self.lib.weights(wr if routed else None, weights.get("router_bias") if routed else None,
                                    w1 if routed else None, weights.get("w3") if routed else None,
@@ -117,6 +120,7 @@ class MoELayer:
         out = torch.empty((T, self.d), dtype=out_dtype or self.out_dtype, device=self.device)
         dims = self.dims
         if out_dtype is not None and _DT[out_dtype] != dims.out_dtype:
-            dims = self.lib.dims(self.d, self.E, self.f, self.fs, self.k, dims.dtype, _DT[out_dtype], self.capacity)
+            dims = self.lib.dims(self.d, self.E, self.f, self.fs, self.k, dims.dtype, _DT[out_dtype], self.capacity,
+                                 self.n_group, self.topk_group)
         self.lib.combine(dims, T, y_rows, y_shared, topk_w, token_row, out)
         return out

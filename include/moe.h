@@ -52,7 +52,9 @@
  *   - Faults inside a kernel surface at the caller's next synchronisation.
  *
  * Limits: 1 <= top_k <= 16; 1 <= n_routed <= 1024; top_k <= n_routed (or
- * n_routed == top_k == 0 for a dense layer); capacity >= 0;
+ * n_routed == top_k == 0 for a dense layer); capacity >= 0; with n_group > 1:
+ * n_group <= 64, n_routed % n_group == 0, 1 <= topk_group <= n_group and
+ * topk_group * (n_routed / n_group) >= top_k;
  * d_model and d_ff (and d_ff_shared when non-zero) multiples of 64;
  * 64 <= d_model <= 32768; T * top_k < 2^31.  On the bf16 prefill path every
  * matrix the expert GEMMs read (u, the [T*k, f] and [T, f_s] hidden
@@ -92,6 +94,9 @@ typedef struct moe_dims {
   int32_t out_dtype;   /* moe_dtype of `out` (MOE_F32 recommended) */
   int32_t capacity;    /* seats per routed expert per call; 0 = no limit.  A caller
                           with a capacity factor cf uses ceil(cf * T * top_k / n_routed). */
+  int32_t n_group;     /* group-limited routing: experts form n_group contiguous groups
+                          (0 or 1 = no groups) ... */
+  int32_t topk_group;  /* ... of which each token keeps topk_group (see moe_router_topk) */
 } moe_dims;
 
 /* Device pointers to the layer's weights (layouts above).  router_bias may be
@@ -140,8 +145,16 @@ moe_status moe_workspace_size(const moe_dims *dims, int64_t T, size_t *bytes);
  * expert index; the selection and slot order equal those of the exact real
  * logits of the stored inputs) and topk_w [T, k] fp32 = the full-softmax
  * probability of each kept expert.
+ * With n_group > 1 and topk_group < n_group the top-k is group-limited: the
+ * experts form n_group contiguous groups of n_routed / n_group, a group scores
+ * its best expert's logit, each token keeps its topk_group best groups (ties to
+ * the lower group) and its k experts are the top-k of those groups' experts;
+ * the gates stay full-softmax probabilities.
  * Source: "What is an 'expert', really?" (glossary: router, top-k, softmax;
- * panel 2) and "Shared Expert" (How it works: the N_r centroids). */
+ * panel 2) and "Shared Expert" (How it works: the N_r centroids); node-limited
+ * routing: "Shared and fine-grained experts" (Developer level, 'Why not go
+ * finer still'; Researcher level, Systems limits: n_group 8, topk_group 4; the
+ * group score is not on the pages). */
 moe_status moe_router_topk(const moe_dims *dims, int64_t T, const void *u, const void *w_router,
                            const float *router_bias, int32_t *topk_idx, float *topk_w,
                            void *ws, size_t ws_bytes, void *stream);

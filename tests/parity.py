@@ -69,13 +69,13 @@ def run_stages(layer, u, path: int):
                 out_stages=out_stages, routed=routed, out=out, diag=diag)
 
 
-def oracle_outputs(u64, toks, a, k, idx_o, token_row_o, capacity):
+def oracle_outputs(u64, toks, a, k, idx_o, token_row_o, capacity, groups=(None, None)):
     """Oracle layer output and routed-only part for the tokens toks.  With a
     capacity, which pairs keep a seat depends on the whole batch: the kept mask
     comes from the oracle's permutation of all tokens, and a dropped pair's gate
     is zeroed (its expert output then adds exactly nothing)."""
     r = oracle.forward(u64[toks], a["w_router"], a["w1"], a["w3"], a["w2"], k, a["bias"],
-                       a["w1s"], a["w3s"], a["w2s"])
+                       a["w1s"], a["w3s"], a["w2s"], n_group=groups[0], topk_group=groups[1])
     assert np.array_equal(r["topk_idx"], idx_o[toks])
     if not capacity:
         return r["out"], r["routed"]
@@ -91,12 +91,13 @@ def check_case(layer, inp, wl: workloads.Workload, path: int = 0, sample: Option
     u = inp["u"]
     T = u.shape[0]
     cap = getattr(layer, "capacity", 0) or None
+    groups = (getattr(layer, "n_group", 0) or None, getattr(layer, "topk_group", 0) or None)
     log(f"[parity] {wl.name} T={T} path={path} sample={sample} capacity={cap}")
     g = run_stages(layer, u, path)
     a = oracle_args(inp)
     u64 = workloads.to_f64(u)
     # -- routing, bit-exact on every token
-    idx_o, gw_o, _, n_exact = oracle.route(u64, a["w_router"], wl.top_k, a["bias"])
+    idx_o, gw_o, _, n_exact = oracle.route(u64, a["w_router"], wl.top_k, a["bias"], *groups)
     idx_g = g["idx"].cpu().numpy()
     bad = np.nonzero((idx_g != idx_o).any(axis=1))[0]
     assert bad.size == 0, (f"top-k differs on {bad.size} tokens, first {bad[:5]}: gpu {idx_g[bad[:3]]} "
@@ -114,7 +115,7 @@ def check_case(layer, inp, wl: workloads.Workload, path: int = 0, sample: Option
     assert torch.equal(g["out"], g["out_stages"])
     # -- outputs
     toks = np.arange(T) if sample is None else workloads.sample_tokens(T, sample, seed)
-    want_out, want_routed = oracle_outputs(u64, toks, a, wl.top_k, idx_o, token_row_o, cap)
+    want_out, want_routed = oracle_outputs(u64, toks, a, wl.top_k, idx_o, token_row_o, cap, groups)
     out_g = g["out"][torch.from_numpy(toks).to(u.device)].to(torch.float64).cpu().numpy()
     routed_g = g["routed"][torch.from_numpy(toks).to(u.device)].to(torch.float64).cpu().numpy()
     e_out = rel_err(out_g, want_out)

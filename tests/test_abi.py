@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_struct_sizes_match_header():
-    assert ctypes.sizeof(B.Dims) == 32
+    assert ctypes.sizeof(B.Dims) == 40
     assert ctypes.sizeof(B.Weights) == 64
     assert ctypes.sizeof(B.Diag) == 16
 
@@ -62,6 +62,11 @@ def _dims(lib, **kw):
     (dict(d_ff_shared=-64), B.MOE_ERR_INVALID_VALUE),
     (dict(n_routed=0, top_k=0, d_ff_shared=0), B.MOE_ERR_INVALID_VALUE),  # a dense layer needs its MLP
     (dict(capacity=-1), B.MOE_ERR_INVALID_VALUE),
+    (dict(n_group=3, topk_group=1), B.MOE_ERR_INVALID_VALUE),   # 8 experts do not split into 3 groups
+    (dict(n_group=4, topk_group=0), B.MOE_ERR_INVALID_VALUE),
+    (dict(n_group=4, topk_group=5), B.MOE_ERR_INVALID_VALUE),
+    (dict(n_group=8, topk_group=1), B.MOE_ERR_INVALID_VALUE),   # one expert per group, top-2 needs 2 groups
+    (dict(n_routed=128, n_group=128, topk_group=2), B.MOE_ERR_UNSUPPORTED),
 ])
 def test_bad_dims(lib, kw, status):
     with pytest.raises(fgr.MoeError) as ei:

@@ -225,3 +225,54 @@ def test_capacity_full_size_sampled(lib):
     C = capacity_seats(1.0, wl.T, wl.top_k, wl.n_routed)
     r = check_case(_layer(inp, wl, capacity=C), inp, wl, sample=128)
     log(f"[capacity] dsv3_prefill C={C}: {r['dropped']} pairs dropped")
+
+
+# ---------------------------------------------------------- group-limited top-k
+GROUPS = [
+    ("dsv3_prefill", 300, 8, 4, PATH_PREFILL),
+    ("dsv3_decode", None, 8, 4, PATH_DECODE),
+    ("skew512", 517, 8, 2, PATH_PREFILL),
+    ("dsmoe16b", 333, 4, 1, PATH_PREFILL),
+    ("eqbudget_fine", None, 8, 3, PATH_PREFILL),
+    ("skew128_top1", 400, 16, 1, PATH_PREFILL),
+]
+
+
+@pytest.mark.parametrize("name,T,ng,tg,path", GROUPS, ids=[f"{c[0]}-T{c[1]}-g{c[2]}x{c[3]}-p{c[4]}" for c in GROUPS])
+def test_group_limited_parity(lib, name, T, ng, tg, path):
+    wl = workloads.get(name)
+    if T is not None:
+        wl = wl.with_T(T)
+    inp = gpu_inputs(wl, seed=9)
+    layer = _layer(inp, wl, n_group=ng, topk_group=tg)
+    check_case(layer, inp, wl, path=path)
+    idx = layer.router_topk(inp["u"])[0].cpu().numpy()
+    G = wl.n_routed // ng
+    assert max(len({int(e) // G for e in row}) for row in idx) <= tg
+
+
+def test_group_limit_changes_routing_at_the_deepseek_v3_shape(lib):
+    wl = workloads.get("dsv3_prefill").with_T(512)
+    inp = gpu_inputs(wl, seed=10)
+    plain = _layer(inp, wl).router_topk(inp["u"])[0]
+    grouped = _layer(inp, wl, n_group=8, topk_group=4).router_topk(inp["u"])[0]
+    all_groups = _layer(inp, wl, n_group=8, topk_group=8).router_topk(inp["u"])[0]
+    torch.cuda.synchronize()
+    changed = int((plain != grouped).any(dim=1).sum())
+    log(f"[groups] dsv3 T=512: {changed} tokens routed differently under 8 groups / keep 4")
+    assert changed > 0 and torch.equal(plain, all_groups)
+    assert torch.equal(plain[:, 0], grouped[:, 0])  # the best expert is always kept
+
+
+def test_group_limit_with_every_logit_tied(lib):
+    # zero router: all keys tie, the walk meets expert 0 first, so group 0 is kept first
+    wl = workloads.Workload("tie_groups", 100, 256, 64, 128, 1, 6, "bf16", None, "tie_groups", "edge case")
+    inp = gpu_inputs(wl)
+    inp["w_router"].zero_()
+    check_case(_layer(inp, wl, n_group=16, topk_group=2), inp, wl, path=PATH_PREFILL)
+
+
+def test_group_limit_full_size_sampled(lib):
+    wl = workloads.get("dsv3_prefill")
+    inp = gpu_inputs(wl, seed=0)
+    check_case(_layer(inp, wl, n_group=8, topk_group=4), inp, wl, sample=128)
