@@ -133,8 +133,14 @@ struct WsLayout {
   size_t y_rows;      // f32 [R, d]
   size_t y_sh;        // f32 [T, d]
   size_t u_norm;      // dtype [T, d] RMS-normalised input (block forward only)
+  size_t dense_part;  // f32 split-reduction partials of the dense decode path (dense bf16 layers only)
   size_t total;
 };
+
+// Dense decode path: rows per pass and reduction splits (gate/up, down).
+#define MOE_DD_ROWS 256
+#define MOE_DD_SPLIT_GU 4
+#define MOE_DD_SPLIT_DN 8
 
 static inline size_t moe_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -165,6 +171,11 @@ static inline WsLayout moe_ws_layout(const moe_dims &dm, int64_t T) {
   L.y_rows = take(R * d * 4);
   L.y_sh = take((size_t)T * d * 4);
   L.u_norm = take((size_t)T * d * hbytes);
+  {
+    const size_t rows = (size_t)(T < MOE_DD_ROWS ? T : MOE_DD_ROWS);
+    const size_t gu = (size_t)MOE_DD_SPLIT_GU * rows * 2 * fs, dn = (size_t)MOE_DD_SPLIT_DN * rows * d;
+    L.dense_part = take(E == 0 && dm.dtype == MOE_BF16 ? 4 * (gu > dn ? gu : dn) : 0);
+  }
   L.total = o;
   return L;
 }

@@ -179,6 +179,172 @@ __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeArgs a) {
   }
 }
 
+// ------------------------------------------------------- dense layers (no routed experts)
+// The dense prefix layers' FFN streams one weight set for all T tokens, so
+// each wave takes every row of a pass (up to 4 x 16 rows, one weight fragment
+// feeding all of them) for NT 16-column tiles, and a slice of the reduction.
+// The token rows are re-read from L2 by every column tile; NT tiles per wave
+// keep that traffic equal to the weight traffic (4 row fragments against NT =
+// 4 weight fragments, or 2 x 2 for gate/up).  Work-groups are single waves, so
+// that the column tiles times S reduction slices give enough of them to fill
+// the chip at decode sizes.  Each slice writes fp32 partial sums
+// P[s][row][col]; a second kernel adds the S partials in slice order (fixed,
+// so the result is deterministic) and applies SiLU(gate) * up (bf16 H) or
+// writes Y.  Gate/up partials hold the gate columns at [0, N) and the up
+// columns at [N, 2N).
+#define DD_U 2  // 32-deep steps per load batch
+
+template <bool GATEUP, int MT, int NT>
+__global__ __launch_bounds__(64) void dense_decode_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W1,
+                                                          const uint16_t *__restrict__ W3, int rows, int K, int N,
+                                                          int ksl, float *__restrict__ P) {
+  const int lane = threadIdx.x;
+  const int n0 = blockIdx.x * 16 * NT;
+  const int s = blockIdx.y;
+  const int r0 = blockIdx.z * 64;
+  const int k_begin = s * ksl, k_end = min(K, k_begin + ksl);
+  const int kofs = (lane >> 4) * 8;  // this lane's 8-element slice of a 32-deep step
+  const uint16_t *ap[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) ap[m] = A + (int64_t)min(r0 + 16 * m + (lane & 15), rows - 1) * K + kofs;
+  const uint16_t *p1[NT];
+  const uint16_t *p3[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int n = min(n0 + 16 * j + (lane & 15), N - 1);  // clamped: columns >= N are never stored
+    p1[j] = W1 + (int64_t)n * K + kofs;
+    p3[j] = GATEUP ? W3 + (int64_t)n * K + kofs : nullptr;
+  }
+  f32x4_t acc1[MT][NT], acc3[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      acc1[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acc3[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  int k0 = k_begin;
+  for (; k0 + 32 * DD_U <= k_end; k0 += 32 * DD_U) {
+    uint4 av[DD_U][MT], b1[DD_U][NT], b3[DD_U][NT];
+#pragma unroll
+    for (int u = 0; u < DD_U; ++u) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        b1[u][j] = dk_load(p1[j] + k0 + 32 * u);
+        if (GATEUP) b3[u][j] = dk_load(p3[j] + k0 + 32 * u);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) av[u][m] = *(const uint4 *)(ap[m] + k0 + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < DD_U; ++u)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const bf16x8_t a8 = as_bf16x8(av[u][m]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          acc1[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(b1[u][j]), acc1[m][j], 0, 0, 0);
+          if (GATEUP)
+            acc3[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(b3[u][j]), acc3[m][j], 0, 0, 0);
+        }
+      }
+    // keep every load of the batch ahead of its MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x020, DD_U * (MT + NT * (GATEUP ? 2 : 1)), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, DD_U * MT * NT * (GATEUP ? 2 : 1), 0);
+  }
+  for (; k0 < k_end; k0 += 32) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const uint4 b1v = dk_load(p1[j] + k0);
+      const uint4 b3v = GATEUP ? dk_load(p3[j] + k0) : b1v;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const bf16x8_t a8 = as_bf16x8(*(const uint4 *)(ap[m] + k0));
+        acc1[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(b1v), acc1[m][j], 0, 0, 0);
+        if (GATEUP) acc3[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(b3v), acc3[m][j], 0, 0, 0);
+      }
+    }
+  }
+  // lane holds rows 4 * (lane / 16) + q of column lane % 16 of each 16 x 16 tile
+  const int pw = GATEUP ? 2 * N : N;  // partial row width
+  float *ps = P + (int64_t)s * rows * pw;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int col = n0 + 16 * j + (lane & 15);
+    if (col >= N) continue;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = r0 + 16 * m + (lane >> 4) * 4 + q;
+        if (row >= rows) continue;
+        ps[(int64_t)row * pw + col] = acc1[m][j][q];
+        if (GATEUP) ps[(int64_t)row * pw + N + col] = acc3[m][j][q];
+      }
+  }
+}
+
+// Sum of the S partials in slice order; gate/up: H = SiLU(gate) * up in bf16,
+// down: Y in fp32.  Four consecutive columns per thread.
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void dense_reduce_kernel(const float *__restrict__ P, int S, int rows, int N,
+                                                           void *__restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (int64_t)rows * N) return;
+  const int64_t row = i / N;
+  const int col = (int)(i % N);
+  const int pw = GATEUP ? 2 * N : N;
+  float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
+  for (int s = 0; s < S; ++s) {
+    const float *ps = P + ((int64_t)s * rows + row) * pw + col;
+    const float4 a = *(const float4 *)ps;
+    g = make_float4(g.x + a.x, g.y + a.y, g.z + a.z, g.w + a.w);
+    if (GATEUP) {
+      const float4 b = *(const float4 *)(ps + N);
+      u = make_float4(u.x + b.x, u.y + b.y, u.z + b.z, u.w + b.w);
+    }
+  }
+  if (GATEUP) {
+    uint2 pk;
+    pk.x = pack_bf16x2(silu_fast(g.x) * u.x, silu_fast(g.y) * u.y);
+    pk.y = pack_bf16x2(silu_fast(g.z) * u.z, silu_fast(g.w) * u.w);
+    *(uint2 *)((uint16_t *)out + row * N + col) = pk;
+  } else {
+    *(float4 *)((float *)out + row * N + col) = g;
+  }
+}
+
+template <bool GATEUP, int NT>
+static void launch_dense_pass(const uint16_t *A, const uint16_t *W1, const uint16_t *W3, int rows, int K, int N,
+                              int S, float *P, void *out, hipStream_t st) {
+  const int ksl = ((K / 32 + S - 1) / S) * 32;  // k per slice, a multiple of 32 (a slice past K adds zeros)
+  const dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)S, (unsigned)((rows + 63) / 64));
+  const int mt = (std::min(rows, 64) + 15) / 16;  // 16-row blocks of a full 64-row group
+  if (mt >= 4) dense_decode_kernel<GATEUP, 4, NT><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+  else if (mt == 3) dense_decode_kernel<GATEUP, 3, NT><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+  else if (mt == 2) dense_decode_kernel<GATEUP, 2, NT><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+  else dense_decode_kernel<GATEUP, 1, NT><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+  const int64_t n4 = (int64_t)rows * N / 4;
+  dense_reduce_kernel<GATEUP><<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, st>>>(P, S, rows, N, out);
+}
+
+// The dense layer on the decode path, in passes of up to MOE_DD_ROWS rows.
+static hipError_t launch_dense_decode(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w, float *y_sh,
+                                      const WsLayout &L, char *ws, hipStream_t st, hipEvent_t ev_mid) {
+  const int d = dm.d_model, fs = dm.d_ff_shared;
+  uint16_t *Hs = (uint16_t *)(ws + L.h_sh);
+  float *P = (float *)(ws + L.dense_part);
+  for (int64_t r0 = 0; r0 < T; r0 += MOE_DD_ROWS) {
+    const int rows = (int)std::min<int64_t>(MOE_DD_ROWS, T - r0);
+    launch_dense_pass<true, 2>((const uint16_t *)u + r0 * d, (const uint16_t *)w.w1s, (const uint16_t *)w.w3s, rows,
+                               d, fs, MOE_DD_SPLIT_GU, P, Hs + r0 * fs, st);
+    if (ev_mid && r0 + MOE_DD_ROWS >= T) (void)hipEventRecord(ev_mid, st);
+    launch_dense_pass<false, 4>(Hs + r0 * fs, (const uint16_t *)w.w2s, nullptr, rows, fs, d, MOE_DD_SPLIT_DN, P,
+                                y_sh + r0 * d, st);
+  }
+  return hipGetLastError();
+}
+
 static int64_t dk_mtile_bound(int64_t R, int E) { return (R + DK_BM - 1) / DK_BM + std::min<int64_t>(E, R); }
 
 hipError_t launch_ffn_decode(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w,
@@ -186,6 +352,7 @@ hipError_t launch_ffn_decode(const moe_dims &dm, int64_t T, const void *u, const
                              float *y_rows, float *y_sh, const WsLayout &L, char *ws, hipStream_t st,
                              hipEvent_t ev_mid) {
   (void)counts;
+  if (dm.n_routed == 0) return launch_dense_decode(dm, T, u, w, y_sh, L, ws, st, ev_mid);
   const int E = dm.n_routed, d = dm.d_model, f = dm.d_ff, fs = dm.d_ff_shared;
   const int hs = fs > 0 ? 1 : 0;
   const int64_t R = T * dm.top_k;

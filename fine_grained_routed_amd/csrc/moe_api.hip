@@ -130,14 +130,15 @@ static moe_status check_opts(const moe_options *o) {
   return MOE_OK;
 }
 
-// Which expert-FFN kernels run: 1 prefill, 2 decode.  A dense layer streams
-// its single weight set per 16 rows on the decode path, so it switches to the
-// tiled GEMMs at a smaller T than a routed layer, whose experts see about
-// T*k/N_r rows each.
+// Which expert-FFN kernels run: 1 prefill, 2 decode.  A dense layer's decode
+// kernels stream its single weight set once per pass of up to 64 rows and
+// take the tiled GEMMs beyond 128 tokens (measured crossover at the
+// DeepSeek-V3 dense shape); a routed layer's experts see about T*k/N_r rows
+// each.
 static int pick_path(const moe_dims &dm, int64_t T, const moe_options *o) {
   const int want = o ? o->path : 0;
   if (want != 0) return want;
-  if (dm.n_routed == 0) return T <= 32 ? 2 : 1;
+  if (dm.n_routed == 0) return T <= 128 ? 2 : 1;
   return (T * dm.top_k <= 2 * (int64_t)dm.n_routed && T <= 256) ? 2 : 1;
 }
 
@@ -155,6 +156,12 @@ struct EventHook {
     return (o && o->events && i < o->n_events) ? (hipEvent_t)o->events[i] : nullptr;
   }
 };
+
+// The tile prefixes are read by every FFN kernel except the dense layers'
+// decode kernels.
+static bool needs_tile_offsets(const moe_dims &dm, int64_t T, const moe_options *o) {
+  return !(dm.n_routed == 0 && dm.dtype == MOE_BF16 && pick_path(dm, T, o) == 2);
+}
 
 // The bf16 prefill GEMMs address their operands through buffer resources
 // with 32-bit byte offsets: every matrix they read must stay under 4 GiB.
@@ -231,7 +238,7 @@ static moe_status run_layer(const moe_dims &dm, int64_t T, const void *u, const 
     ev.rec(1);
     ev.rec(2);
   }
-  MOE_TRY_HIP(launch_tile_offsets(dm, T, counts, L, w, st), "tile offsets");
+  if (needs_tile_offsets(dm, T, opts)) MOE_TRY_HIP(launch_tile_offsets(dm, T, counts, L, w, st), "tile offsets");
   ev.rec(3);
   MOE_CHECK(run_ffn(dm, T, u, wts, counts, offsets, row_token, y_rows, y_sh, opts, L, w, st, ev.get(4)));
   ev.rec(5);
@@ -316,7 +323,8 @@ moe_status moe_expert_ffn(const moe_dims *dims, int64_t T, const void *u, const 
   MOE_CHECK(check_path_limits(*dims, T, opts));
   hipStream_t st = (hipStream_t)stream;
   EventHook ev{opts, st};
-  MOE_TRY_HIP(launch_tile_offsets(*dims, T, counts, L, (char *)ws, st), "tile offsets");
+  if (needs_tile_offsets(*dims, T, opts))
+    MOE_TRY_HIP(launch_tile_offsets(*dims, T, counts, L, (char *)ws, st), "tile offsets");
   ev.rec(0);
   MOE_CHECK(run_ffn(*dims, T, u, *wts, counts, offsets, row_token, y_rows, y_shared, opts, L, (char *)ws, st,
                     ev.get(1)));
