@@ -38,9 +38,9 @@
 // The grid covers an upper bound of the tile count; each work-group reads the
 // device-side tile prefixes (256-row tiles), so no host sync is needed.
 // Work-groups are dispatched round-robin over the 8 XCDs.  The tile order
-// (described in the kernel) is cut into chunks of PF_CHUNK consecutive tiles,
-// dealt to the XCDs in turn: work-group i, the (i / 8)-th of XCD i % 8, takes
-// tile (((i / 8) / PF_CHUNK) * 8 + i % 8) * PF_CHUNK + (i / 8) % PF_CHUNK.  The
+// (described in the kernel) is cut into chunks of CH consecutive tiles (64 for
+// gate/up, 32 for down), dealt to the XCDs in turn: work-group i, the (i / 8)-th
+// of XCD i % 8, takes tile (((i / 8) / CH) * 8 + i % 8) * CH + (i / 8) % CH.  The
 // 32 CUs of an XCD work through one chunk at a time, mostly one expert,
 // sharing its token rows and weight panels in that XCD's L2, and every XCD
 // receives an even share of full and ragged tiles.
@@ -55,7 +55,8 @@
 #define PF_BM_IDX 4  // moe_bm_of(4) == 256
 #define PF_WM 4      // 32-row sub-tiles per wave (2 x 2 waves over 8 sub-tiles)
 #define PF_GM 8      // m-tiles per ordering block (routed experts)
-#define PF_CHUNK 64  // consecutive tiles dealt to one XCD
+#define PF_CHUNK_GU 64  // consecutive tiles dealt to one XCD (gate/up)
+#define PF_CHUNK_DN 32  // consecutive tiles dealt to one XCD (down; 3.22 against 3.73 ms for the dense layer's)
 #define PF_GM_SH 4   // m-tiles per ordering block (shared group)
 #define PF_LOADS 8   // DMA instructions per wave per operand per k-tile (8 rows of 128 B each)
 
@@ -329,8 +330,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
   const int mt_s = a.tile_off[a.E + 1] - mt_r;
   const int64_t tiles_r = (int64_t)mt_r * a.nt_r;
   const int64_t total = tiles_r + (int64_t)mt_s * a.nt_s;
+  constexpr int CH = GATEUP ? PF_CHUNK_GU : PF_CHUNK_DN;
   const int64_t slot = blockIdx.x >> 3;
-  const int64_t tile = ((slot / PF_CHUNK) * 8 + (blockIdx.x & 7)) * PF_CHUNK + slot % PF_CHUNK;
+  const int64_t tile = ((slot / CH) * 8 + (blockIdx.x & 7)) * CH + slot % CH;
   if (tile >= total) return;
 
   bool shared;
@@ -504,8 +506,8 @@ static int64_t mtile_bound(int64_t R, int E) { return (R + PF_BM - 1) / PF_BM + 
 
 // Work-groups covering `tiles` under the chunked XCD deal: whole rounds of 8
 // chunks, so that every tile index below `tiles` has a work-group.
-static int64_t pf_grid(int64_t tiles) {
-  const int64_t round = 8 * PF_CHUNK;
+static int64_t pf_grid(int64_t tiles, int chunk) {
+  const int64_t round = 8 * (int64_t)chunk;
   return (tiles + round - 1) / round * round;
 }
 
@@ -543,7 +545,7 @@ hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u,
   g1.has_shared = hs;
   g1.nt_r = (f + PF_BN / 2 - 1) / (PF_BN / 2);
   g1.nt_s = hs ? (fs + PF_BN / 2 - 1) / (PF_BN / 2) : 1;
-  const int64_t grid1 = pf_grid(mtile_bound(R, E) * g1.nt_r + mt_sh * g1.nt_s);
+  const int64_t grid1 = pf_grid(mtile_bound(R, E) * g1.nt_r + mt_sh * g1.nt_s, PF_CHUNK_GU);
   grouped_gemm_bf16_kernel<true><<<dim3((unsigned)grid1), 256, 0, st>>>(g1);
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
 
@@ -568,7 +570,7 @@ hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u,
   g2.has_shared = hs;
   g2.nt_r = (d + PF_BN - 1) / PF_BN;
   g2.nt_s = g2.nt_r;
-  const int64_t grid2 = pf_grid(mtile_bound(R, E) * g2.nt_r + mt_sh * g2.nt_s);
+  const int64_t grid2 = pf_grid(mtile_bound(R, E) * g2.nt_r + mt_sh * g2.nt_s, PF_CHUNK_DN);
   grouped_gemm_bf16_kernel<false><<<dim3((unsigned)grid2), 256, 0, st>>>(g2);
   return hipGetLastError();
 }
