@@ -233,12 +233,19 @@ static moe_status run_layer(const moe_dims &dm, int64_t T, const void *u, const 
     ev.rec(1);
     MOE_TRY_HIP(launch_topk(dm, T, u, wts.w_router, wts.router_bias, idx, gw, L, w, st), "top-k");
     ev.rec(2);
-    MOE_TRY_HIP(launch_permute(dm, T, idx, counts, offsets, row_token, token_row, L, w, st), "permute");
+    if (T <= MOE_PERM_BLOCK) {  // one launch for the permutation and the tile prefixes
+      MOE_TRY_HIP(launch_permute_small(dm, T, idx, counts, offsets, row_token, token_row,
+                                       (int32_t *)(w + L.tile_off), L, w, st),
+                  "permute");
+    } else {
+      MOE_TRY_HIP(launch_permute(dm, T, idx, counts, offsets, row_token, token_row, L, w, st), "permute");
+      MOE_TRY_HIP(launch_tile_offsets(dm, T, counts, L, w, st), "tile offsets");
+    }
   } else {
     ev.rec(1);
     ev.rec(2);
+    if (needs_tile_offsets(dm, T, opts)) MOE_TRY_HIP(launch_tile_offsets(dm, T, counts, L, w, st), "tile offsets");
   }
-  if (needs_tile_offsets(dm, T, opts)) MOE_TRY_HIP(launch_tile_offsets(dm, T, counts, L, w, st), "tile offsets");
   ev.rec(3);
   MOE_CHECK(run_ffn(dm, T, u, wts, counts, offsets, row_token, y_rows, y_sh, opts, L, w, st, ev.get(4)));
   ev.rec(5);

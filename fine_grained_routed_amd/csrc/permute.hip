@@ -133,8 +133,104 @@ __global__ __launch_bounds__(MOE_PERM_BLOCK) void perm_scatter_kernel(const int3
   }
 }
 
+// The whole permutation for T <= MOE_PERM_BLOCK tokens (one block) in one
+// work-group of 1024 threads, and, when tile_off is given, the GEMM tile
+// prefixes too: at decode sizes the four launches cost more than their work.
+// Same results as the three kernels above and tile_offsets_kernel below.
+__global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restrict__ idx, int64_t T, int E, int k,
+                                                          int cap, int has_shared, int32_t *__restrict__ counts,
+                                                          int32_t *__restrict__ offsets,
+                                                          int32_t *__restrict__ row_token,
+                                                          int32_t *__restrict__ token_row,
+                                                          int32_t *__restrict__ tile_off, DiagWords *diag) {
+  extern __shared__ unsigned long long bm[];  // [E][PERM_WORDS] bitmap, then int[E] group starts
+  int *start = (int *)(bm + E * PERM_WORDS);
+  __shared__ int sh[1024];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * PERM_WORDS; i += 1024) bm[i] = 0ull;
+  __syncthreads();
+  if (tid < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(int64_t)tid * k + j];
+      if (e < 0 || e >= E) {
+        atomicOr(&diag->flags, MOE_DIAG_BAD_INDEX);
+        continue;
+      }
+      const unsigned long long bit = 1ull << (tid & 63);
+      const unsigned long long old = atomicOr(&bm[e * PERM_WORDS + (tid >> 6)], bit);
+      if (old & bit) atomicOr(&diag->flags, MOE_DIAG_DUPLICATE);
+    }
+  }
+  __syncthreads();
+  int tot = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int q = 0; q < PERM_WORDS; ++q) tot += __popcll(bm[tid * PERM_WORDS + q]);
+  }
+  const int seats = (cap > 0 && tot > cap) ? cap : tot;
+  int all;
+  const int off = block_exclusive_scan(tid < E ? seats : 0, sh, &all);
+  if (tid < E) {
+    counts[tid] = seats;
+    offsets[tid] = off;
+    start[tid] = off;
+  }
+  if (tid == 0) offsets[E] = all;
+  if (tile_off) {
+    for (int b = 0; b < MOE_N_BM; ++b) {
+      const int bmh = moe_bm_of(b);
+      int tiles;
+      const int toff = block_exclusive_scan(tid < E ? (seats + bmh - 1) / bmh : 0, sh, &tiles);
+      int32_t *to = tile_off + b * (E + 2);
+      if (tid < E) to[tid] = toff;
+      if (tid == 0) {
+        to[E] = tiles;
+        to[E + 1] = tiles + (has_shared ? (int)((T + bmh - 1) / bmh) : 0);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < T) {
+    const int w = tid >> 6;
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[(int64_t)tid * k + j];
+      if (e < 0 || e >= E) {
+        token_row[(int64_t)tid * k + j] = -1;
+        continue;
+      }
+      const unsigned long long *row = bm + e * PERM_WORDS;
+      int rank = 0;
+#pragma unroll
+      for (int q = 0; q < PERM_WORDS; ++q)
+        if (q < w) rank += __popcll(row[q]);
+      rank += __popcll((tid & 63) ? (row[w] & ((1ull << (tid & 63)) - 1ull)) : 0ull);
+      if (cap > 0 && rank >= cap) {
+        token_row[(int64_t)tid * k + j] = -1;  // no seat left
+        continue;
+      }
+      const int r = start[e] + rank;
+      token_row[(int64_t)tid * k + j] = r;
+      row_token[r] = tid;
+    }
+  }
+}
+
+// Permutation of T <= MOE_PERM_BLOCK tokens in one launch; tile_off (or NULL)
+// receives the tile prefixes as launch_tile_offsets would.
+hipError_t launch_permute_small(const moe_dims &dm, int64_t T, const int32_t *topk_idx, int32_t *counts,
+                                int32_t *offsets, int32_t *row_token, int32_t *token_row, int32_t *tile_off,
+                                const WsLayout &L, char *ws, hipStream_t st) {
+  const int E = dm.n_routed;
+  const size_t lds = (size_t)E * PERM_WORDS * sizeof(unsigned long long) + (size_t)E * sizeof(int);
+  perm_small_kernel<<<1, 1024, lds, st>>>(topk_idx, T, E, dm.top_k, dm.capacity, dm.d_ff_shared > 0 ? 1 : 0, counts,
+                                          offsets, row_token, token_row, tile_off, (DiagWords *)(ws + L.diag));
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const moe_dims &dm, int64_t T, const int32_t *topk_idx, int32_t *counts, int32_t *offsets,
                           int32_t *row_token, int32_t *token_row, const WsLayout &L, char *ws, hipStream_t st) {
+  if (T <= MOE_PERM_BLOCK)
+    return launch_permute_small(dm, T, topk_idx, counts, offsets, row_token, token_row, nullptr, L, ws, st);
   const int E = dm.n_routed, k = dm.top_k;
   const int64_t nblk = (T + MOE_PERM_BLOCK - 1) / MOE_PERM_BLOCK;
   int32_t *blk = (int32_t *)(ws + L.blk);
