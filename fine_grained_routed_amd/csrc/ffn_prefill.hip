@@ -246,10 +246,12 @@ __device__ __forceinline__ void post_barrier_hint() {
 // stage of tile j, now free.  Past the end the last tile is re-fetched into
 // stages nobody reads again, so every iteration issues the same DMA and one
 // constant wait publishes the next tile: when it runs, only the weight tile
-// issued in this iteration may be in flight.
+// issued in this iteration may be in flight.  A wave without token-tile DMA
+// (adma false: its rows are past the tile's valid sub-tiles) issues the weight
+// DMA alone, and the same wait still leaves only that tile in flight.
 template <int MW, int SA, int SB>
 __device__ __forceinline__ void k_iter(const Operand &A, const Operand &B, const WaveRows &w, int j, int nk,
-                                       Frags<MW> &f0, Frags<MW> &f1, f32x16_t (&acc)[PF_WM][4]) {
+                                       Frags<MW> &f0, Frags<MW> &f1, f32x16_t (&acc)[PF_WM][4], bool adma) {
   const int kb = min(j + 2, nk - 1);
   if (MW > 0) read_frags<MW, SA, SB>(f1, w, 1);
   issue_op<0, 3>(B, stage_b<(SB + 2) % 3>(), kb);
@@ -273,7 +275,7 @@ __device__ __forceinline__ void k_iter(const Operand &A, const Operand &B, const
   // step-0 fragments of tile j + 1 (after the last tile this reads stages
   // whose values are never used; reading LDS is always in bounds)
   if (MW > 0) read_frags<MW, SA ^ 1, (SB + 1) % 3>(f0, w, 0);
-  issue_op(A, stage_a<SA>(), min(j + 2, nk - 1));
+  if (adma) issue_op(A, stage_a<SA>(), min(j + 2, nk - 1));
   if (MW > 0) {
     mfma_step<MW>(f1, acc);
     post_barrier_hint<MW>();
@@ -282,36 +284,39 @@ __device__ __forceinline__ void k_iter(const Operand &A, const Operand &B, const
 
 // The k loop of one tile for a wave with MW valid 32-row sub-tiles
 // (compile-time, so the body is straight-line).  Every wave of the
-// work-group, whatever its MW, issues the same DMA and barriers.
+// work-group, whatever its MW, issues the same weight-tile DMA and barriers;
+// token-tile DMA only when some of its 64 rows are read (adma).
 template <int MW>
 __device__ __forceinline__ void k_loop(const Operand &A, const Operand &B, const WaveRows &w, int K,
-                                       f32x16_t (&acc)[PF_WM][4]) {
+                                       f32x16_t (&acc)[PF_WM][4], bool adma) {
   const int nk = K / PF_BK;
   // prologue: A tiles 0, 1 and B tiles 0, 1 (clamped), issued in the order the
   // loop's constant wait assumes
-  issue_op(A, stage_a<0>(), 0);
+  if (adma) issue_op(A, stage_a<0>(), 0);
   issue_op(B, stage_b<0>(), 0);
   issue_op(B, stage_b<1>(), min(1, nk - 1));
-  issue_op(A, stage_a<1>(), min(1, nk - 1));
-  publish<2 * PF_LOADS>();  // A0 and B0 landed
+  if (adma) issue_op(A, stage_a<1>(), min(1, nk - 1));
+  // A0 and B0 landed (a wave without token DMA has only B1 left in flight)
+  if (adma) publish<2 * PF_LOADS>();
+  else publish<PF_LOADS>();
   Frags<MW> f0, f1;
   if (MW > 0) read_frags<MW, 0, 0>(f0, w, 0);
   // six k-tiles per trip (the stage pattern repeats every lcm(2, 3) tiles);
   // whole trips are unconditional, the remainder follows
   int j = 0;
   for (; j + 6 <= nk; j += 6) {
-    k_iter<MW, 0, 0>(A, B, w, j, nk, f0, f1, acc);
-    k_iter<MW, 1, 1>(A, B, w, j + 1, nk, f0, f1, acc);
-    k_iter<MW, 0, 2>(A, B, w, j + 2, nk, f0, f1, acc);
-    k_iter<MW, 1, 0>(A, B, w, j + 3, nk, f0, f1, acc);
-    k_iter<MW, 0, 1>(A, B, w, j + 4, nk, f0, f1, acc);
-    k_iter<MW, 1, 2>(A, B, w, j + 5, nk, f0, f1, acc);
+    k_iter<MW, 0, 0>(A, B, w, j, nk, f0, f1, acc, adma);
+    k_iter<MW, 1, 1>(A, B, w, j + 1, nk, f0, f1, acc, adma);
+    k_iter<MW, 0, 2>(A, B, w, j + 2, nk, f0, f1, acc, adma);
+    k_iter<MW, 1, 0>(A, B, w, j + 3, nk, f0, f1, acc, adma);
+    k_iter<MW, 0, 1>(A, B, w, j + 4, nk, f0, f1, acc, adma);
+    k_iter<MW, 1, 2>(A, B, w, j + 5, nk, f0, f1, acc, adma);
   }
-  if (j < nk) k_iter<MW, 0, 0>(A, B, w, j, nk, f0, f1, acc);
-  if (j + 1 < nk) k_iter<MW, 1, 1>(A, B, w, j + 1, nk, f0, f1, acc);
-  if (j + 2 < nk) k_iter<MW, 0, 2>(A, B, w, j + 2, nk, f0, f1, acc);
-  if (j + 3 < nk) k_iter<MW, 1, 0>(A, B, w, j + 3, nk, f0, f1, acc);
-  if (j + 4 < nk) k_iter<MW, 0, 1>(A, B, w, j + 4, nk, f0, f1, acc);
+  if (j < nk) k_iter<MW, 0, 0>(A, B, w, j, nk, f0, f1, acc, adma);
+  if (j + 1 < nk) k_iter<MW, 1, 1>(A, B, w, j + 1, nk, f0, f1, acc, adma);
+  if (j + 2 < nk) k_iter<MW, 0, 2>(A, B, w, j + 2, nk, f0, f1, acc, adma);
+  if (j + 3 < nk) k_iter<MW, 1, 0>(A, B, w, j + 3, nk, f0, f1, acc, adma);
+  if (j + 4 < nk) k_iter<MW, 0, 1>(A, B, w, j + 4, nk, f0, f1, acc, adma);
   // the trailing re-fetches must land before the work-group can exit
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
@@ -434,12 +439,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
+  // a wave whose 64 token-tile rows all lie past the tile's valid sub-tiles
+  // skips their DMA: nobody reads those LDS rows
+  const bool adma = 64 * wvu < 32 * ns;
   // branch-free main loop per count of valid sub-tiles of this wave
-  if (mw == 4) k_loop<4>(A, B, w, K, acc);
-  else if (mw == 3) k_loop<3>(A, B, w, K, acc);
-  else if (mw == 2) k_loop<2>(A, B, w, K, acc);
-  else if (mw == 1) k_loop<1>(A, B, w, K, acc);
-  else k_loop<0>(A, B, w, K, acc);
+  if (mw == 4) k_loop<4>(A, B, w, K, acc, adma);
+  else if (mw == 3) k_loop<3>(A, B, w, K, acc, adma);
+  else if (mw == 2) k_loop<2>(A, B, w, K, acc, adma);
+  else if (mw == 1) k_loop<1>(A, B, w, K, acc, adma);
+  else k_loop<0>(A, B, w, K, acc, adma);
 
   // ---- epilogue.  32x32 accumulator layout (transposed product): register
   // 4q + c of lane l holds token row l % 32 of the sub-tile and output column
