@@ -79,22 +79,30 @@ class HipEvents:
         return out.value
 
 
-def timed_steps(step, steps, warmup, hev, stages=STAGES):
+def timed_steps(step, steps, warmup, hev, stages=STAGES, between=None, per_step=None):
     """Time `steps` calls of step(events) after `warmup` untimed ones; the library
-    records len(stages) + 1 events per call at its stage boundaries."""
+    records len(stages) + 1 events per call at its stage boundaries.  between()
+    (if given) runs after every call, outside the events; per_step (a list, if
+    given) receives each call's event-measured total."""
     import torch
     for _ in range(warmup):
         step(None)
+        if between:
+            between()
     evs = [hev.create(len(stages) + 1) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
         step(evs[s])
+        if between:
+            between()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     stage = {name: sum(hev.ms(e[i], e[i + 1]) for e in evs) / steps for i, name in enumerate(stages)}
-    total = sum(hev.ms(e[0], e[len(stages)]) for e in evs) / steps
-    return wall_ms, total, stage
+    totals = [hev.ms(e[0], e[len(stages)]) for e in evs]
+    if per_step is not None:
+        per_step.extend(totals)
+    return wall_ms, sum(totals) / steps, stage
 
 
 def cpu_baseline(wl, inp, n_tokens, block=False):
@@ -141,6 +149,9 @@ def main():
                     help="seat limit ceil(CF * T * k / N_r) per expert (0: no limit)")
     ap.add_argument("--groups", default="", metavar="NG,TG",
                     help="group-limited routing: NG expert groups, TG kept per token (e.g. 8,4)")
+    ap.add_argument("--flush-mb", type=int, default=0, metavar="MB",
+                    help="write an MB-sized scratch buffer between timed steps (outside the events), so that "
+                         "small layers are timed without their weights in the 256 MB last-level cache")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens the oracle baseline runs on (default: 64 for the MoE layer, 16384 dense)")
@@ -187,8 +198,14 @@ def main():
         T = u.shape[0]
         stages = STAGES
         step = lambda ev: layer.forward(u, path=PATH_AUTO, events=ev)
+    between = None
+    if args.flush_mb:
+        scratch = torch.empty(args.flush_mb << 18, dtype=torch.float32, device="cuda")
+        between = lambda: scratch.fill_(1.0)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    wall_ms, ev_ms, stage = timed_steps(step, args.steps, args.warmup, hev, stages)
+    per_step = []
+    wall_ms, ev_ms, stage = timed_steps(step, args.steps, args.warmup, hev, stages, between, per_step)
+    per_step.sort()
 
     R = T * wl.top_k
     gu_flop = 4.0 * wl.d * (R * wl.d_ff + T * wl.d_ff_shared)
@@ -239,6 +256,9 @@ def main():
         "layer_frac_of_peak": total_flop / (wall_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stage_ms": stage,
         "event_ms_per_step": ev_ms,
+        "event_ms_median": per_step[len(per_step) // 2],
+        "event_ms_min": per_step[0],
+        "flush_mb_between_steps": args.flush_mb,
         "down_tflops": dn_flop / (stage["down"] * 1e-3) / 1e12,
     }
     if args.block:
