@@ -119,7 +119,7 @@ struct WsLayout {
   size_t logits;      // double [T, N_r]
   size_t logit_part;  // double [S, T, N_r] router partial sums (S = router_splits > 1 only)
   size_t unorm2;      // double [T]   squared 2-norm of each token row
-  size_t wnorm2;      // double [N_r] squared 2-norm of each router row
+  size_t wnorm;       // double [N_r] 2-norm of each router row
   size_t blk;         // int32  [nblk, N_r] per-block histograms, then bases
   size_t tile_off;    // int32  [MOE_N_BM, N_r + 2] per-expert m-tile prefixes (+ shared)
   size_t h;           // bf16 or f32 [R, f] routed hidden activations
@@ -157,7 +157,7 @@ static inline WsLayout moe_ws_layout(const moe_dims &dm, int64_t T) {
   const int S = router_splits(dm, T);
   L.logit_part = take(S > 1 ? (size_t)S * T * E * 8 : 0);
   L.unorm2 = take((size_t)T * 8);
-  L.wnorm2 = take(E * 8);
+  L.wnorm = take(E * 8);
   L.blk = take(nblk * E * 4);
   L.tile_off = take((size_t)MOE_N_BM * (E + 2) * 4);
   L.h = take(R * f * hbytes);

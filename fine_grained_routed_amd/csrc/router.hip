@@ -27,8 +27,8 @@
 #define RT_LDS_STRIDE (RT_BK + 8)  // bf16 elements per LDS row (16-byte pad)
 
 // ------------------------------------------------------------------ row norms
-// out[r] = sum_i x[r,i]^2 in fp64 (one wave per row).
-template <bool BF16>
+// out[r] = sum_i x[r,i]^2 in fp64 (one wave per row), or its square root (ROOT).
+template <bool BF16, bool ROOT = false>
 __global__ __launch_bounds__(256) void row_norm2_kernel(const void *__restrict__ x, int64_t rows, int d,
                                                         double *__restrict__ out) {
   const int lane = threadIdx.x & 63;
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void row_norm2_kernel(const void *__restrict__
     }
   }
   s = wave_sum_f64(s);
-  if (lane == 0) out[r] = s;
+  if (lane == 0) out[r] = ROOT ? sqrt(s) : s;
 }
 
 // -------------------------------------------------------- bf16 logits (MFMA)
@@ -222,10 +222,10 @@ hipError_t launch_router_logits(const moe_dims &dm, int64_t T, const void *u, co
   const int E = dm.n_routed, d = dm.d_model;
   double *logits = (double *)(ws + L.logits);
   double *un2 = (double *)(ws + L.unorm2);
-  double *wn2 = (double *)(ws + L.wnorm2);
+  double *wn = (double *)(ws + L.wnorm);
   if (dm.dtype == MOE_BF16) {
     row_norm2_kernel<true><<<dim3((unsigned)((T + 3) / 4)), 256, 0, st>>>(u, T, d, un2);
-    row_norm2_kernel<true><<<dim3((unsigned)((E + 3) / 4)), 256, 0, st>>>(w_router, E, d, wn2);
+    row_norm2_kernel<true, true><<<dim3((unsigned)((E + 3) / 4)), 256, 0, st>>>(w_router, E, d, wn);
     const int nk = d / RT_BK;
     const int S = router_splits(dm, T);
     const int kps = (nk + S - 1) / S;
@@ -239,7 +239,7 @@ hipError_t launch_router_logits(const moe_dims &dm, int64_t T, const void *u, co
     }
   } else {
     row_norm2_kernel<false><<<dim3((unsigned)((T + 3) / 4)), 256, 0, st>>>(u, T, d, un2);
-    row_norm2_kernel<false><<<dim3((unsigned)((E + 3) / 4)), 256, 0, st>>>(w_router, E, d, wn2);
+    row_norm2_kernel<false, true><<<dim3((unsigned)((E + 3) / 4)), 256, 0, st>>>(w_router, E, d, wn);
     dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16));
     router_logits_f32_kernel<<<grid, 256, 0, st>>>((const float *)u, (const float *)w_router, bias, T, E, d, logits);
   }

@@ -159,7 +159,7 @@ __device__ __forceinline__ int lowest_expert(unsigned bits) {
 
 template <int S, bool BF16>
 __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ logits, const double *__restrict__ un2,
-                                                   const double *__restrict__ wn2, const float *__restrict__ bias,
+                                                   const double *__restrict__ wn, const float *__restrict__ bias,
                                                    const void *__restrict__ u, const void *__restrict__ w,
                                                    int64_t T, int E, int d, int k, double c1, int G,
                                                    int topk_group, int32_t *__restrict__ idx_out,
@@ -170,13 +170,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
   double L[S], B[S];
   unsigned avail = 0;
   const double unorm = un2[t];
+  const double su = sqrt(unorm);  // ||u_t||; wn[e] = ||c_e|| (the (1 + 2^-30) factor covers their rounding)
   const double NEG = -__builtin_huge_val();
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int e = lane + 64 * s;
     if (e < E) {
       L[s] = logits[t * E + e];
-      B[s] = c1 * sqrt(unorm * wn2[e]) * (1.0 + 0x1p-30) + 0x1p-50 * fabs(L[s]) + d * 0x1p-120;
+      B[s] = c1 * su * wn[e] * (1.0 + 0x1p-30) + 0x1p-50 * fabs(L[s]) + d * 0x1p-120;
       avail |= 1u << s;
     } else {
       L[s] = NEG;
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
   double sum = 0.0;
 #pragma unroll
   for (int s = 0; s < S; ++s)
-    if (avail & (1u << s)) sum += exp(L[s] - mx);
+    if (avail & (1u << s)) sum += (double)expf((float)(L[s] - mx));
   sum = wave_sum_f64(sum);
 
   const void *urow = BF16 ? (const void *)((const uint16_t *)u + t * d) : (const void *)((const float *)u + t * d);
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
         // (expert e lives in lane e % 64, register slot e / 64)
         for (int e = lowest_expert(need); e != 0x7fffffff; e = lowest_expert(need)) {
           const double l64 = dot_f64<BF16>(urow, w, bias, e, d);
-          const double b64 = c64 * sqrt(unorm * wn2[e]) * (1.0 + 0x1p-30) + 0x1p-51 * fabs(l64) + d * 0x1p-120;
+          const double b64 = c64 * su * wn[e] * (1.0 + 0x1p-30) + 0x1p-51 * fabs(l64) + d * 0x1p-120;
 #pragma unroll
           for (int s = 0; s < S; ++s)
             if (lane + 64 * s == e) {
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
     lw = wave_max_f64(lw);
     if (lane == 0) {
       idx_out[t * k + j] = win;
-      w_out[t * k + j] = (float)(exp(lw - mx) / sum);
+      w_out[t * k + j] = (float)((double)expf((float)(lw - mx)) / sum);
     }
   }
   if (lane == 0) {
@@ -328,16 +329,16 @@ static void launch_topk_s(const moe_dims &dm, int64_t T, const void *u, const vo
   dim3 grid((unsigned)((T + TOPK_TOKENS_PER_WG - 1) / TOPK_TOKENS_PER_WG));
   const double *lg = (const double *)(ws + L.logits);
   const double *un2 = (const double *)(ws + L.unorm2);
-  const double *wn2 = (const double *)(ws + L.wnorm2);
+  const double *wn = (const double *)(ws + L.wnorm);
   DiagWords *diag = (DiagWords *)(ws + L.diag);
   // group size, or 0 when routing is not group-limited
   const bool grouped = dm.n_group > 1 && dm.topk_group < dm.n_group;
   const int G = grouped ? dm.n_routed / dm.n_group : 0;
   if (dm.dtype == MOE_BF16)
-    topk_kernel<S, true><<<grid, 256, 0, st>>>(lg, un2, wn2, bias, u, w, T, dm.n_routed, dm.d_model, dm.top_k, c1,
+    topk_kernel<S, true><<<grid, 256, 0, st>>>(lg, un2, wn, bias, u, w, T, dm.n_routed, dm.d_model, dm.top_k, c1,
                                                G, dm.topk_group, idx, wout, diag);
   else
-    topk_kernel<S, false><<<grid, 256, 0, st>>>(lg, un2, wn2, bias, u, w, T, dm.n_routed, dm.d_model, dm.top_k, c1,
+    topk_kernel<S, false><<<grid, 256, 0, st>>>(lg, un2, wn, bias, u, w, T, dm.n_routed, dm.d_model, dm.top_k, c1,
                                                 G, dm.topk_group, idx, wout, diag);
 }
 
