@@ -180,22 +180,136 @@ __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------- dense layers (no routed experts)
-// The dense prefix layers' FFN streams one weight set for all T tokens, so
-// each wave takes every row of a pass (up to 4 x 16 rows, one weight fragment
-// feeding all of them) for NT 16-column tiles, and a slice of the reduction.
-// The token rows are re-read from L2 by every column tile; NT tiles per wave
-// keep that traffic equal to the weight traffic (4 row fragments against NT =
-// 4 weight fragments, or 2 x 2 for gate/up).  Work-groups are single waves, so
-// that the column tiles times S reduction slices give enough of them to fill
-// the chip at decode sizes.  Each slice writes fp32 partial sums
+// The dense prefix layers' FFN streams one weight set for all T tokens, so a
+// work-group takes every row of a pass (up to 4 x 16 rows, so one weight
+// fragment feeds all of them), 64 NT output columns (4 waves of NT 16-column
+// tiles) and one of S slices of the reduction (S slices times the column
+// groups give enough work-groups to fill the chip at decode sizes).  The
+// token rows of each 64-deep batch are staged once into LDS for the four
+// waves (double-buffered, chunks XOR-swizzled per row so the fragment reads
+// are free of bank conflicts); each wave streams its own weight fragments
+// into registers one batch ahead.  Each slice writes fp32 partial sums
 // P[s][row][col]; a second kernel adds the S partials in slice order (fixed,
 // so the result is deterministic) and applies SiLU(gate) * up (bf16 H) or
 // writes Y.  Gate/up partials hold the gate columns at [0, N) and the up
 // columns at [N, 2N).
+#define DD_BK 64  // reduction depth per batch (two 32-deep MFMA steps)
+
+template <bool GATEUP, int MT, int NT>
+__global__ __launch_bounds__(256) void dense_decode_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W1,
+                                                           const uint16_t *__restrict__ W3, int rows, int K, int N,
+                                                           int ksl, float *__restrict__ P) {
+  __shared__ __attribute__((aligned(16))) uint4 As[2][64 * 8];  // [buffer][row * 8 + slot], 16-byte chunks
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n0 = blockIdx.x * 64 * NT + wv * 16 * NT;
+  const int s = blockIdx.y;
+  const int r0 = blockIdx.z * 64;
+  const int k_begin = s * ksl, k_end = min(K, k_begin + ksl);
+  const int nb = max(0, (k_end - k_begin) / DD_BK);  // batches (a slice past K has none)
+  // cooperative token-tile load: thread tid moves chunks tid and tid + 256 of
+  // the 64 x 8 chunks of a batch (row c / 8, chunk c % 8)
+  const uint16_t *ag[2];
+  int aslot[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = tid + 256 * q, row = c >> 3, ch = c & 7;
+    ag[q] = A + (int64_t)min(r0 + row, rows - 1) * K + k_begin + ch * 8;  // clamped: rows past the pass are never stored
+    aslot[q] = row * 8 + (ch ^ (row & 7));
+  }
+  // the wave's weight rows
+  const int kofs = (lane >> 4) * 8;  // this lane's 8-element slice of a 32-deep step
+  const uint16_t *p1[NT];
+  const uint16_t *p3[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int n = min(n0 + 16 * j + (lane & 15), N - 1);  // clamped: columns >= N are never stored
+    p1[j] = W1 + (int64_t)n * K + k_begin + kofs;
+    p3[j] = GATEUP ? W3 + (int64_t)n * K + k_begin + kofs : nullptr;
+  }
+  f32x4_t acc1[MT][NT], acc3[MT][NT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      acc1[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acc3[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  uint4 ar0 = make_uint4(0u, 0u, 0u, 0u), ar1 = ar0;  // the next batch's two token chunks of this thread
+  uint4 bc1[2][NT], bc3[2][NT], bn1[2][NT], bn3[2][NT];
+  if (nb > 0) {
+    ar0 = *(const uint4 *)ag[0];
+    ar1 = *(const uint4 *)ag[1];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        bc1[u][j] = dk_load(p1[j] + 32 * u);
+        bc3[u][j] = GATEUP ? dk_load(p3[j] + 32 * u) : bc1[u][j];
+      }
+  }
+  for (int b = 0; b < nb; ++b) {
+    uint4 *buf = As[b & 1];
+    buf[aslot[0]] = ar0;
+    buf[aslot[1]] = ar1;
+    __syncthreads();  // batch b's token tile is in LDS (and batch b's weights in registers)
+    const int bn = min(b + 1, nb - 1);  // the last batch re-loads its own data (in bounds, unused)
+    ar0 = *(const uint4 *)(ag[0] + bn * DD_BK);
+    ar1 = *(const uint4 *)(ag[1] + bn * DD_BK);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        bn1[u][j] = dk_load(p1[j] + bn * DD_BK + 32 * u);
+        bn3[u][j] = GATEUP ? dk_load(p3[j] + bn * DD_BK + 32 * u) : bn1[u][j];
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int row = 16 * m + (lane & 15), ch = 4 * u + (lane >> 4);
+        const bf16x8_t a8 = as_bf16x8(buf[row * 8 + (ch ^ (row & 7))]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          acc1[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(bc1[u][j]), acc1[m][j], 0, 0, 0);
+          if (GATEUP)
+            acc3[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(bc3[u][j]), acc3[m][j], 0, 0, 0);
+        }
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        bc1[u][j] = bn1[u][j];
+        bc3[u][j] = bn3[u][j];
+      }
+  }
+  // lane holds rows 4 * (lane / 16) + q of column lane % 16 of each 16 x 16 tile
+  const int pw = GATEUP ? 2 * N : N;  // partial row width
+  float *ps = P + (int64_t)s * rows * pw;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int col = n0 + 16 * j + (lane & 15);
+    if (col >= N) continue;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = r0 + 16 * m + (lane >> 4) * 4 + q;
+        if (row >= rows) continue;
+        ps[(int64_t)row * pw + col] = acc1[m][j][q];
+        if (GATEUP) ps[(int64_t)row * pw + N + col] = acc3[m][j][q];
+      }
+  }
+}
+
+// Small passes (under 48 rows): single-wave work-groups, each with every row
+// of the pass for NT 16-column tiles, re-reading the token fragments from L2
+// (as many bytes as its weight fragments); staging them in LDS does not pay
+// for its barriers at this size.
 #define DD_U 2  // 32-deep steps per load batch
 
 template <bool GATEUP, int MT, int NT>
-__global__ __launch_bounds__(64) void dense_decode_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W1,
+__global__ __launch_bounds__(64) void dense_decode_wave_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W1,
                                                           const uint16_t *__restrict__ W3, int rows, int K, int N,
                                                           int ksl, float *__restrict__ P) {
   const int lane = threadIdx.x;
@@ -317,13 +431,19 @@ __global__ __launch_bounds__(256) void dense_reduce_kernel(const float *__restri
 template <bool GATEUP, int NT>
 static void launch_dense_pass(const uint16_t *A, const uint16_t *W1, const uint16_t *W3, int rows, int K, int N,
                               int S, float *P, void *out, hipStream_t st) {
-  const int ksl = ((K / 32 + S - 1) / S) * 32;  // k per slice, a multiple of 32 (a slice past K adds zeros)
-  const dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)S, (unsigned)((rows + 63) / 64));
   const int mt = (std::min(rows, 64) + 15) / 16;  // 16-row blocks of a full 64-row group
-  if (mt >= 4) dense_decode_kernel<GATEUP, 4, NT><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
-  else if (mt == 3) dense_decode_kernel<GATEUP, 3, NT><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
-  else if (mt == 2) dense_decode_kernel<GATEUP, 2, NT><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
-  else dense_decode_kernel<GATEUP, 1, NT><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+  if (mt >= 3) {
+    // k per slice: whole 64-deep batches (K is a multiple of 64; a slice past K adds zeros)
+    const int ksl = ((K / DD_BK + S - 1) / S) * DD_BK;
+    const dim3 grid((unsigned)((N + 64 * NT - 1) / (64 * NT)), (unsigned)S, (unsigned)((rows + 63) / 64));
+    if (mt >= 4) dense_decode_kernel<GATEUP, 4, NT><<<grid, 256, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+    else dense_decode_kernel<GATEUP, 3, NT><<<grid, 256, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+  } else {
+    const int ksl = ((K / 32 + S - 1) / S) * 32;  // k per slice, a multiple of 32 (a slice past K adds zeros)
+    const dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)S, 1);
+    if (mt == 2) dense_decode_wave_kernel<GATEUP, 2, NT><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+    else dense_decode_wave_kernel<GATEUP, 1, NT><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+  }
   const int64_t n4 = (int64_t)rows * N / 4;
   dense_reduce_kernel<GATEUP><<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, st>>>(P, S, rows, N, out);
 }

@@ -132,13 +132,13 @@ static moe_status check_opts(const moe_options *o) {
 
 // Which expert-FFN kernels run: 1 prefill, 2 decode.  A dense layer's decode
 // kernels stream its single weight set once per pass of up to 64 rows and
-// take the tiled GEMMs beyond 128 tokens (measured crossover at the
+// take the tiled GEMMs beyond 256 tokens (measured crossover at the
 // DeepSeek-V3 dense shape); a routed layer's experts see about T*k/N_r rows
 // each.
 static int pick_path(const moe_dims &dm, int64_t T, const moe_options *o) {
   const int want = o ? o->path : 0;
   if (want != 0) return want;
-  if (dm.n_routed == 0) return T <= 128 ? 2 : 1;
+  if (dm.n_routed == 0) return T <= 256 ? 2 : 1;
   return (T * dm.top_k <= 2 * (int64_t)dm.n_routed && T <= 256) ? 2 : 1;
 }
 

@@ -120,7 +120,7 @@ typedef struct moe_weights {
  *   2..7 as 1..6 above (moe_block_forward), or 0 start, 1 after gate/up,
  *   2 after down (moe_expert_ffn).  Boundaries beyond n_events are not
  *   recorded.
- *   The automatic choice for a dense layer is the decode path when T <= 128. */
+ *   The automatic choice for a dense layer is the decode path when T <= 256. */
 typedef struct moe_options {
   int32_t path;
   int32_t n_events;

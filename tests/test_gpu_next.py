@@ -59,6 +59,7 @@ DENSE = [
     ("dense_small", 32, PATH_AUTO),
     ("dense_small", 63, PATH_AUTO),
     ("dense_small", 129, PATH_AUTO),
+    ("dense_small", 257, PATH_AUTO),
     ("dense_small", 257, PATH_PREFILL),
     ("dense_small_f32", None, PATH_AUTO),
     ("dsv3_dense_prefill", 300, PATH_PREFILL),
