@@ -197,9 +197,12 @@ hipError_t launch_tile_offsets(const moe_dims &dm, int64_t T, const int32_t *cou
 hipError_t launch_permute_small(const moe_dims &dm, int64_t T, const int32_t *topk_idx, int32_t *counts,
                                 int32_t *offsets, int32_t *row_token, int32_t *token_row, int32_t *tile_off,
                                 const WsLayout &L, char *ws, hipStream_t st);
-hipError_t launch_ffn_prefill(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w,
-                              const int32_t *offsets, const int32_t *row_token, float *y_rows, float *y_sh,
-                              const WsLayout &L, char *ws, hipStream_t st, hipEvent_t ev_mid);
+hipError_t launch_ffn_f32(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w, const int32_t *offsets,
+                          const int32_t *row_token, float *y_rows, float *y_sh, const WsLayout &L, char *ws,
+                          hipStream_t st, hipEvent_t ev_mid);
+hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w,
+                                   const int32_t *offsets, const int32_t *row_token, float *y_rows, float *y_sh,
+                                   const WsLayout &L, char *ws, hipStream_t st, hipEvent_t ev_mid);
 hipError_t launch_ffn_decode(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w,
                              const int32_t *counts, const int32_t *offsets, const int32_t *row_token,
                              float *y_rows, float *y_sh, const WsLayout &L, char *ws, hipStream_t st,

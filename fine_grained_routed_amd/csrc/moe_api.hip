@@ -8,13 +8,6 @@
 
 #include "common.h"
 
-hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w,
-                                   const int32_t *offsets, const int32_t *row_token, float *y_rows, float *y_sh,
-                                   const WsLayout &L, char *ws, hipStream_t st, hipEvent_t ev_mid);
-hipError_t launch_ffn_f32(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w, const int32_t *offsets,
-                          const int32_t *row_token, float *y_rows, float *y_sh, const WsLayout &L, char *ws,
-                          hipStream_t st, hipEvent_t ev_mid);
-
 static thread_local char g_err[512] = "";
 
 static moe_status fail(moe_status s, const char *fmt, ...) {
