@@ -137,12 +137,53 @@ struct WsLayout {
   size_t total;
 };
 
-// Dense decode path: rows per pass and reduction splits (gate/up, down).
+// Dense decode path: rows per pass; tile widths and reduction slices.
 #define MOE_DD_ROWS 256
-#define MOE_DD_SPLIT_GU 4
-#define MOE_DD_SPLIT_DN 8
+#ifndef MOE_DD_SPLIT_GU
+#define MOE_DD_SPLIT_GU 4  // reduction slices of the single-wave kernel (passes under 33 rows), gate/up
+#endif
+#ifndef MOE_DD_SPLIT_DN
+#define MOE_DD_SPLIT_DN 8  // the same for the down pass
+#endif
+#define MOE_DD_SPLIT_MAX 8
+#ifndef MOE_DD_WG_GU
+#define MOE_DD_WG_GU 1152  // work-groups the four-wave kernel aims at (slices x column groups x row blocks), gate/up
+#endif
+#ifndef MOE_DD_WG_DN
+#define MOE_DD_WG_DN 448  // the same for the down pass
+#endif
+#ifndef MOE_DD_NT_GU
+#define MOE_DD_NT_GU 1  // 16-column tiles per wave of the four-wave kernel, gate/up (each of gate and up)
+#endif
+#ifndef MOE_DD_NT_DN
+#define MOE_DD_NT_DN 2  // the same for the down pass
+#endif
+#ifndef MOE_DD_UL_GU
+#define MOE_DD_UL_GU 4  // 32-deep steps per batch of the four-wave dense decode kernel (gate/up)
+#endif
+#ifndef MOE_DD_UL_DN
+#define MOE_DD_UL_DN 2  // the same for the down pass
+#endif
 
 static inline size_t moe_align(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Whether a dense decode pass of `rows` rows runs the four-wave kernel (three
+// or more 16-row blocks) rather than the single-wave one.
+static inline bool moe_dd_four_wave(int rows) { return ((rows < 64 ? rows : 64) + 15) / 16 >= 3; }
+
+// Reduction slices of a dense decode pass of `rows` rows with N output
+// columns: the four-wave kernel takes as many as give about MOE_DD_WG_*
+// work-groups in all (1 to MOE_DD_SPLIT_MAX), the single-wave kernel a fixed
+// count.
+static inline int moe_dd_splits(bool gateup, int64_t N, int rows) {
+  if (!moe_dd_four_wave(rows)) return gateup ? MOE_DD_SPLIT_GU : MOE_DD_SPLIT_DN;
+  const int64_t cols = 64 * (gateup ? MOE_DD_NT_GU : MOE_DD_NT_DN);
+  const int64_t wg = (N + cols - 1) / cols * ((rows + 63) / 64);
+  if (wg <= 0) return 1;
+  const int64_t target = gateup ? MOE_DD_WG_GU : MOE_DD_WG_DN;
+  const int64_t s = (target + wg / 2) / wg;
+  return (int)(s < 1 ? 1 : s > MOE_DD_SPLIT_MAX ? MOE_DD_SPLIT_MAX : s);
+}
 
 static inline WsLayout moe_ws_layout(const moe_dims &dm, int64_t T) {
   WsLayout L;
@@ -171,10 +212,17 @@ static inline WsLayout moe_ws_layout(const moe_dims &dm, int64_t T) {
   L.y_rows = take(R * d * 4);
   L.y_sh = take((size_t)T * d * 4);
   L.u_norm = take((size_t)T * d * hbytes);
-  {
-    const size_t rows = (size_t)(T < MOE_DD_ROWS ? T : MOE_DD_ROWS);
-    const size_t gu = (size_t)MOE_DD_SPLIT_GU * rows * 2 * fs, dn = (size_t)MOE_DD_SPLIT_DN * rows * d;
-    L.dense_part = take(E == 0 && dm.dtype == MOE_BF16 ? 4 * (gu > dn ? gu : dn) : 0);
+  {  // the partials of the largest pass: a full one, or the last (shorter) one
+    size_t need = 0;
+    const int64_t cand[2] = {T < MOE_DD_ROWS ? T : MOE_DD_ROWS, T % MOE_DD_ROWS};
+    for (int64_t r : cand) {
+      if (r <= 0 || E != 0 || dm.dtype != MOE_BF16) continue;
+      const size_t gu = (size_t)moe_dd_splits(true, (int64_t)fs, (int)r) * r * 2 * fs;
+      const size_t dn = (size_t)moe_dd_splits(false, (int64_t)d, (int)r) * r * d;
+      need = need > gu ? need : gu;
+      need = need > dn ? need : dn;
+    }
+    L.dense_part = take(E == 0 && dm.dtype == MOE_BF16 ? 4 * need : 0);
   }
   L.total = o;
   return L;

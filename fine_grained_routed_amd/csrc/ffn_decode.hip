@@ -183,38 +183,42 @@ __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeArgs a) {
 // The dense prefix layers' FFN streams one weight set for all T tokens, so a
 // work-group takes every row of a pass (up to 4 x 16 rows, so one weight
 // fragment feeds all of them), 64 NT output columns (4 waves of NT 16-column
-// tiles) and one of S slices of the reduction (S slices times the column
-// groups give enough work-groups to fill the chip at decode sizes).  The
-// token rows of each 64-deep batch are staged once into LDS for the four
+// tiles) and one of S slices of the reduction (S is chosen per pass so that
+// slices x column groups x row blocks come to a set number of work-groups,
+// enough to fill the chip at decode sizes).  The token rows of each batch
+// (32 UL deep) are staged once into LDS for the four
 // waves (double-buffered, chunks XOR-swizzled per row so the fragment reads
 // are free of bank conflicts); each wave streams its own weight fragments
 // into registers one batch ahead.  Each slice writes fp32 partial sums
 // P[s][row][col]; a second kernel adds the S partials in slice order (fixed,
 // so the result is deterministic) and applies SiLU(gate) * up (bf16 H) or
 // writes Y.  Gate/up partials hold the gate columns at [0, N) and the up
-// columns at [N, 2N).
-#define DD_BK 64  // reduction depth per batch (two 32-deep MFMA steps)
-
-template <bool GATEUP, int MT, int NT>
+// columns at [N, 2N).  K is a multiple of the batch depth.
+template <bool GATEUP, int MT, int NT, int UL>
 __global__ __launch_bounds__(256) void dense_decode_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ W1,
                                                            const uint16_t *__restrict__ W3, int rows, int K, int N,
                                                            int ksl, float *__restrict__ P) {
-  __shared__ __attribute__((aligned(16))) uint4 As[2][64 * 8];  // [buffer][row * 8 + slot], 16-byte chunks
+  constexpr int BK = 32 * UL;      // batch depth
+  constexpr int CPR = BK / 8;      // 16-byte chunks per token row of a batch
+  constexpr int CPT = 64 * CPR / 256;  // chunks each thread moves per batch
+  static_assert(UL % 2 == 0, "the slot swizzle needs whole groups of 8 chunks per row");
+  __shared__ __attribute__((aligned(16))) uint4 As[2][64 * CPR];  // [buffer][row * CPR + slot]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n0 = blockIdx.x * 64 * NT + wv * 16 * NT;
   const int s = blockIdx.y;
   const int r0 = blockIdx.z * 64;
   const int k_begin = s * ksl, k_end = min(K, k_begin + ksl);
-  const int nb = max(0, (k_end - k_begin) / DD_BK);  // batches (a slice past K has none)
-  // cooperative token-tile load: thread tid moves chunks tid and tid + 256 of
-  // the 64 x 8 chunks of a batch (row c / 8, chunk c % 8)
-  const uint16_t *ag[2];
-  int aslot[2];
+  const int nb = max(0, (k_end - k_begin) / BK);  // batches (a slice past K has none)
+  // cooperative token-tile load: thread tid moves chunks tid + 256 q of the
+  // 64 x CPR chunks of a batch (row c / CPR, chunk c % CPR); the low three
+  // bits of a chunk's slot are XORed with the row's
+  const uint16_t *ag[CPT];
+  int aslot[CPT];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int c = tid + 256 * q, row = c >> 3, ch = c & 7;
+  for (int q = 0; q < CPT; ++q) {
+    const int c = tid + 256 * q, row = c / CPR, ch = c % CPR;
     ag[q] = A + (int64_t)min(r0 + row, rows - 1) * K + k_begin + ch * 8;  // clamped: rows past the pass are never stored
-    aslot[q] = row * 8 + (ch ^ (row & 7));
+    aslot[q] = row * CPR + (ch ^ (row & 7));
   }
   // the wave's weight rows
   const int kofs = (lane >> 4) * 8;  // this lane's 8-element slice of a 32-deep step
@@ -234,13 +238,15 @@ __global__ __launch_bounds__(256) void dense_decode_kernel(const uint16_t *__res
       acc1[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       acc3[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-  uint4 ar0 = make_uint4(0u, 0u, 0u, 0u), ar1 = ar0;  // the next batch's two token chunks of this thread
-  uint4 bc1[2][NT], bc3[2][NT], bn1[2][NT], bn3[2][NT];
-  if (nb > 0) {
-    ar0 = *(const uint4 *)ag[0];
-    ar1 = *(const uint4 *)ag[1];
+  uint4 ar[CPT];  // the next batch's token chunks of this thread
+  uint4 bc1[UL][NT], bc3[UL][NT], bn1[UL][NT], bn3[UL][NT];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+  for (int q = 0; q < CPT; ++q) ar[q] = make_uint4(0u, 0u, 0u, 0u);
+  if (nb > 0) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) ar[q] = *(const uint4 *)ag[q];
+#pragma unroll
+    for (int u = 0; u < UL; ++u)
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         bc1[u][j] = dk_load(p1[j] + 32 * u);
@@ -249,25 +255,25 @@ __global__ __launch_bounds__(256) void dense_decode_kernel(const uint16_t *__res
   }
   for (int b = 0; b < nb; ++b) {
     uint4 *buf = As[b & 1];
-    buf[aslot[0]] = ar0;
-    buf[aslot[1]] = ar1;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) buf[aslot[q]] = ar[q];
     __syncthreads();  // batch b's token tile is in LDS (and batch b's weights in registers)
     const int bn = min(b + 1, nb - 1);  // the last batch re-loads its own data (in bounds, unused)
-    ar0 = *(const uint4 *)(ag[0] + bn * DD_BK);
-    ar1 = *(const uint4 *)(ag[1] + bn * DD_BK);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int q = 0; q < CPT; ++q) ar[q] = *(const uint4 *)(ag[q] + bn * BK);
+#pragma unroll
+    for (int u = 0; u < UL; ++u)
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        bn1[u][j] = dk_load(p1[j] + bn * DD_BK + 32 * u);
-        bn3[u][j] = GATEUP ? dk_load(p3[j] + bn * DD_BK + 32 * u) : bn1[u][j];
+        bn1[u][j] = dk_load(p1[j] + bn * BK + 32 * u);
+        bn3[u][j] = GATEUP ? dk_load(p3[j] + bn * BK + 32 * u) : bn1[u][j];
       }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < UL; ++u)
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const int row = 16 * m + (lane & 15), ch = 4 * u + (lane >> 4);
-        const bf16x8_t a8 = as_bf16x8(buf[row * 8 + (ch ^ (row & 7))]);
+        const bf16x8_t a8 = as_bf16x8(buf[row * CPR + (ch ^ (row & 7))]);
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
           acc1[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, as_bf16x8(bc1[u][j]), acc1[m][j], 0, 0, 0);
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(256) void dense_decode_kernel(const uint16_t *__res
         }
       }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < UL; ++u)
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         bc1[u][j] = bn1[u][j];
@@ -428,21 +434,31 @@ __global__ __launch_bounds__(256) void dense_reduce_kernel(const float *__restri
   }
 }
 
-template <bool GATEUP, int NT>
+// NT, UL: the four-wave kernel's column tiles per wave and batch depth; NTW:
+// the single-wave kernel's column tiles
+template <bool GATEUP, int NT, int UL, int NTW>
 static void launch_dense_pass(const uint16_t *A, const uint16_t *W1, const uint16_t *W3, int rows, int K, int N,
-                              int S, float *P, void *out, hipStream_t st) {
+                              float *P, void *out, hipStream_t st) {
   const int mt = (std::min(rows, 64) + 15) / 16;  // 16-row blocks of a full 64-row group
-  if (mt >= 3) {
-    // k per slice: whole 64-deep batches (K is a multiple of 64; a slice past K adds zeros)
-    const int ksl = ((K / DD_BK + S - 1) / S) * DD_BK;
+  const int S = moe_dd_splits(GATEUP, N, rows);
+  if (moe_dd_four_wave(rows)) {
+    // k per slice: whole batches (K is a multiple of 64; a slice past K adds zeros)
     const dim3 grid((unsigned)((N + 64 * NT - 1) / (64 * NT)), (unsigned)S, (unsigned)((rows + 63) / 64));
-    if (mt >= 4) dense_decode_kernel<GATEUP, 4, NT><<<grid, 256, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
-    else dense_decode_kernel<GATEUP, 3, NT><<<grid, 256, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+    if (K % (32 * UL) == 0) {
+      constexpr int BK = 32 * UL;
+      const int ksl = ((K / BK + S - 1) / S) * BK;
+      if (mt >= 4) dense_decode_kernel<GATEUP, 4, NT, UL><<<grid, 256, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+      else dense_decode_kernel<GATEUP, 3, NT, UL><<<grid, 256, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+    } else {
+      const int ksl = ((K / 64 + S - 1) / S) * 64;
+      if (mt >= 4) dense_decode_kernel<GATEUP, 4, NT, 2><<<grid, 256, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+      else dense_decode_kernel<GATEUP, 3, NT, 2><<<grid, 256, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+    }
   } else {
     const int ksl = ((K / 32 + S - 1) / S) * 32;  // k per slice, a multiple of 32 (a slice past K adds zeros)
-    const dim3 grid((unsigned)((N + 16 * NT - 1) / (16 * NT)), (unsigned)S, 1);
-    if (mt == 2) dense_decode_wave_kernel<GATEUP, 2, NT><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
-    else dense_decode_wave_kernel<GATEUP, 1, NT><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+    const dim3 grid((unsigned)((N + 16 * NTW - 1) / (16 * NTW)), (unsigned)S, 1);
+    if (mt == 2) dense_decode_wave_kernel<GATEUP, 2, NTW><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
+    else dense_decode_wave_kernel<GATEUP, 1, NTW><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
   }
   const int64_t n4 = (int64_t)rows * N / 4;
   dense_reduce_kernel<GATEUP><<<dim3((unsigned)((n4 + 255) / 256)), 256, 0, st>>>(P, S, rows, N, out);
@@ -456,11 +472,11 @@ static hipError_t launch_dense_decode(const moe_dims &dm, int64_t T, const void 
   float *P = (float *)(ws + L.dense_part);
   for (int64_t r0 = 0; r0 < T; r0 += MOE_DD_ROWS) {
     const int rows = (int)std::min<int64_t>(MOE_DD_ROWS, T - r0);
-    launch_dense_pass<true, 2>((const uint16_t *)u + r0 * d, (const uint16_t *)w.w1s, (const uint16_t *)w.w3s, rows,
-                               d, fs, MOE_DD_SPLIT_GU, P, Hs + r0 * fs, st);
+    launch_dense_pass<true, MOE_DD_NT_GU, MOE_DD_UL_GU, 2>((const uint16_t *)u + r0 * d, (const uint16_t *)w.w1s,
+                                                          (const uint16_t *)w.w3s, rows, d, fs, P, Hs + r0 * fs, st);
     if (ev_mid && r0 + MOE_DD_ROWS >= T) (void)hipEventRecord(ev_mid, st);
-    launch_dense_pass<false, 4>(Hs + r0 * fs, (const uint16_t *)w.w2s, nullptr, rows, fs, d, MOE_DD_SPLIT_DN, P,
-                                y_sh + r0 * d, st);
+    launch_dense_pass<false, MOE_DD_NT_DN, MOE_DD_UL_DN, 2>(Hs + r0 * fs, (const uint16_t *)w.w2s, nullptr, rows, fs, d,
+                                                            P, y_sh + r0 * d, st);
   }
   return hipGetLastError();
 }

@@ -90,6 +90,18 @@ def test_workspace_size_grows_with_T(lib):
     assert lib.workspace_size(d, 1000) > lib.workspace_size(d, 10)
 
 
+@pytest.mark.parametrize("kw", [dict(d_ff_shared=0), dict(n_routed=0, top_k=0, d_ff=0, d_ff_shared=640),
+                                dict(n_routed=0, top_k=0, d_ff=0, d_ff_shared=640, dtype=fgr.MOE_F32),
+                                dict(d_ff_shared=0, dtype=fgr.MOE_F32)])
+def test_workspace_size_of_every_layer_kind(lib, kw):
+    # routed layers without a shared MLP and dense layers (whose decode path
+    # sizes split-reduction partials per pass) at pass boundaries and ragged T
+    d = _dims(lib, **kw)
+    sizes = [lib.workspace_size(d, T) for T in (0, 1, 32, 33, 64, 255, 256, 257, 300, 513, 4096)]
+    assert all(s > 0 for s in sizes)
+    assert sizes[-1] >= sizes[1]
+
+
 def test_T_zero_is_a_noop_even_with_null_pointers(lib):
     d = _dims(lib)
     lib.layer_forward(d, 0, None, lib.weights(), None, None, None, ws_bytes=0, stream=0)

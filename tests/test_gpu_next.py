@@ -75,6 +75,26 @@ def test_dense_ffn_parity(lib, name, T, path):
     _check_dense(wl, gpu_inputs(wl, seed=1), path)
 
 
+# a model width that is an odd multiple of 64 (the gate/up batches fall back to
+# 64-deep ones) and output widths that leave ragged column groups, on passes
+# that take either decode kernel, a ragged 64-row block and a short last pass
+ODD = [20, 33, 64, 100, 300]
+
+
+@pytest.mark.parametrize("T", ODD)
+def test_dense_decode_odd_width(lib, T):
+    import dataclasses
+    wl = dataclasses.replace(workloads.get("dense_small"), name="dense_odd", d=320, d_ff=192, family="dodd", T=T)
+    _check_dense(wl, gpu_inputs(wl, seed=4), PATH_DECODE)
+
+
+@pytest.mark.parametrize("T", [100, 256, 300])
+def test_dense_decode_full_width_sampled(lib, T):
+    # one and two slices per pass, and a 44-row last pass, at the DeepSeek-V3 dense shape
+    wl = workloads.get("dsv3_dense_decode").with_T(T)
+    _check_dense(wl, gpu_inputs(wl, seed=5), PATH_DECODE, sample=16)
+
+
 def test_dense_ffn_bf16_output_and_paths_agree(lib):
     wl = workloads.get("dense_small").with_T(48)
     inp = gpu_inputs(wl, seed=2)
