@@ -32,10 +32,18 @@
 // reduces over the short expert width and keeps more of its single weight in
 // flight per column (measured at DeepSeek-V3 decode: 1.06 ms against 1.17 ms
 // with the gate/up shape).
+#ifndef DK_GU_NT
 #define DK_GU_NT 2
+#endif
+#ifndef DK_GU_U
 #define DK_GU_U 4
+#endif
+#ifndef DK_DN_NT
 #define DK_DN_NT 1
+#endif
+#ifndef DK_DN_U
 #define DK_DN_U 8
+#endif
 constexpr int dk_cols(int nt) { return 16 * nt * DK_WAVES; }  // columns per work-group
 
 struct DecodeArgs {
@@ -52,11 +60,44 @@ struct DecodeArgs {
 };
 
 
-// Weight loads are ordinary (cached) loads: each 128-byte line of a weight row
-// is requested as two 64-byte halves by two instructions, and with
-// non-temporal loads the second half often misses L2 again (measured: 1.7x
-// the weight bytes fetched from memory); cached, it hits.
+// Weight fragments in the matrix-core layout (lane l: row l & 15, 16-byte
+// chunk l / 16 of a 32-deep step) are ordinary cached loads: each 128-byte
+// line of a weight row is then requested as two 64-byte halves by two
+// instructions, and with non-temporal loads the second half often misses L2
+// again (measured: 1.7x the weight bytes fetched); cached, it hits.
 __device__ __forceinline__ uint4 dk_load(const uint16_t *p) { return *(const uint4 *)p; }
+
+// Whole-line weight loads: for each pair of 32-deep steps (a
+// 64-deep window, 128 bytes of every weight row) and each 16-column tile, two
+// non-temporal loads each cover 8 complete rows: lane l of load i reads row
+// 8 i + (l & 7) of the tile, 16-byte chunk 4 * bit3(l) + l / 16 of the window.
+// Swapping the two registers between lanes l and l ^ 8 (within 16-lane rows)
+// where bit 3 of the lane is set then gives each step's operand in the
+// matrix-core layout (row l & 15, chunk l / 16 of the step): step u takes the
+// values that lanes with bit 3 == u loaded.  Every line is fetched once, so
+// these loads are non-temporal: at DeepSeek-V3 decode the routed gate/up runs
+// at 6.7 TB/s this way against 6.0 with cached half-line loads.  (The dense
+// four-wave kernel keeps cached loads: its row blocks share weight lines, and
+// holding raw and exchanged registers cost it occupancy.)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t dk_load_nt(const uint16_t *p) {
+  return __builtin_nontemporal_load((const u32x4_t *)p);
+}
+__device__ __forceinline__ unsigned dk_xor8(unsigned v) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xf, 0xf, false);  // row_ror:8 == lane ^ 8 in 16
+}
+__device__ __forceinline__ void dk_lines_to_steps(const u32x4_t &r0, const u32x4_t &r1, bool hi, uint4 &s0,
+                                                  uint4 &s1) {
+  unsigned o0[4], o1[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const unsigned x0 = dk_xor8(r0[c]), x1 = dk_xor8(r1[c]);
+    o0[c] = hi ? x1 : r0[c];
+    o1[c] = hi ? r1[c] : x0;
+  }
+  s0 = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+  s1 = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+}
 
 template <bool GATEUP, int DK_NT, int DK_UNROLL>
 __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeArgs a) {
@@ -122,20 +163,43 @@ __global__ __launch_bounds__(256) void decode_ffn_kernel(DecodeArgs a) {
     acc1[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     acc3[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  static_assert(DK_UNROLL % 2 == 0, "whole-line loads go by pairs of steps");
+  const bool hi8 = (lane & 8) != 0;
+  const uint16_t *q1[DK_NT][2];
+  const uint16_t *q3[DK_NT][2];
+#pragma unroll
+  for (int j = 0; j < DK_NT; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int n = min(n0 + j * 16 + 8 * i + (lane & 7), N - 1);  // clamped; columns >= N are never stored
+      const int ch = 4 * ((lane >> 3) & 1) + (lane >> 4);
+      q1[j][i] = w1 + (int64_t)n * K + 8 * ch;
+      q3[j][i] = GATEUP ? w3 + (int64_t)n * K + 8 * ch : nullptr;
+    }
   // main loop: DK_UNROLL steps per batch, every load of a batch issued before
   // the first use; remainder: single 32-deep steps
   const int kmain = K - K % (32 * DK_UNROLL);
   for (int k0 = 0; k0 < kmain; k0 += 32 * DK_UNROLL) {
     uint4 av[DK_UNROLL], b1[DK_UNROLL][DK_NT], b3[DK_UNROLL][DK_NT];
+    u32x4_t l1[DK_UNROLL][DK_NT], l3[DK_UNROLL][DK_NT];  // [2 x pair + i][j]
 #pragma unroll
-    for (int s = 0; s < DK_UNROLL; ++s) {
-      av[s] = *(const uint4 *)(ap + k0 + 32 * s);
+    for (int s = 0; s < DK_UNROLL; ++s) av[s] = *(const uint4 *)(ap + k0 + 32 * s);
+#pragma unroll
+    for (int s2 = 0; s2 < DK_UNROLL; s2 += 2)
+#pragma unroll
+      for (int j = 0; j < DK_NT; ++j)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          l1[s2 + i][j] = dk_load_nt(q1[j][i] + k0 + 32 * s2);
+          if (GATEUP) l3[s2 + i][j] = dk_load_nt(q3[j][i] + k0 + 32 * s2);
+        }
+#pragma unroll
+    for (int s2 = 0; s2 < DK_UNROLL; s2 += 2)
 #pragma unroll
       for (int j = 0; j < DK_NT; ++j) {
-        b1[s][j] = dk_load(p1[j] + k0 + 32 * s);
-        if (GATEUP) b3[s][j] = dk_load(p3[j] + k0 + 32 * s);
+        dk_lines_to_steps(l1[s2][j], l1[s2 + 1][j], hi8, b1[s2][j], b1[s2 + 1][j]);
+        if (GATEUP) dk_lines_to_steps(l3[s2][j], l3[s2 + 1][j], hi8, b3[s2][j], b3[s2 + 1][j]);
       }
-    }
 #pragma unroll
     for (int s = 0; s < DK_UNROLL; ++s) {
       const bf16x8_t a8 = as_bf16x8(av[s]);
@@ -343,18 +407,39 @@ __global__ __launch_bounds__(64) void dense_decode_wave_kernel(const uint16_t *_
       acc1[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       acc3[m][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+  // whole-line weight loads by pairs of 32-deep steps (lane layout as in dk_lines_to_steps)
+  static_assert(DD_U == 2, "one pair of steps per batch");
+  const bool hi8 = (lane & 8) != 0;
+  const uint16_t *q1[NT][2];
+  const uint16_t *q3[NT][2];
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int n = min(n0 + 16 * j + 8 * i + (lane & 7), N - 1);  // clamped: columns >= N are never stored
+      const int ch = 4 * ((lane >> 3) & 1) + (lane >> 4);
+      q1[j][i] = W1 + (int64_t)n * K + 8 * ch;
+      q3[j][i] = GATEUP ? W3 + (int64_t)n * K + 8 * ch : nullptr;
+    }
   int k0 = k_begin;
   for (; k0 + 32 * DD_U <= k_end; k0 += 32 * DD_U) {
     uint4 av[DD_U][MT], b1[DD_U][NT], b3[DD_U][NT];
+    u32x4_t l1[2][NT], l3[2][NT];
 #pragma unroll
-    for (int u = 0; u < DD_U; ++u) {
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        b1[u][j] = dk_load(p1[j] + k0 + 32 * u);
-        if (GATEUP) b3[u][j] = dk_load(p3[j] + k0 + 32 * u);
+      for (int i = 0; i < 2; ++i) {
+        l1[i][j] = dk_load_nt(q1[j][i] + k0);
+        if (GATEUP) l3[i][j] = dk_load_nt(q3[j][i] + k0);
       }
 #pragma unroll
+    for (int u = 0; u < DD_U; ++u)
+#pragma unroll
       for (int m = 0; m < MT; ++m) av[u][m] = *(const uint4 *)(ap[m] + k0 + 32 * u);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      dk_lines_to_steps(l1[0][j], l1[1][j], hi8, b1[0][j], b1[1][j]);
+      if (GATEUP) dk_lines_to_steps(l3[0][j], l3[1][j], hi8, b3[0][j], b3[1][j]);
     }
 #pragma unroll
     for (int u = 0; u < DD_U; ++u)
@@ -455,7 +540,7 @@ static void launch_dense_pass(const uint16_t *A, const uint16_t *W1, const uint1
       else dense_decode_kernel<GATEUP, 3, NT, 2><<<grid, 256, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
     }
   } else {
-    const int ksl = ((K / 32 + S - 1) / S) * 32;  // k per slice, a multiple of 32 (a slice past K adds zeros)
+    const int ksl = ((K / 64 + S - 1) / S) * 64;  // k per slice, whole 128-byte lines (a slice past K adds zeros)
     const dim3 grid((unsigned)((N + 16 * NTW - 1) / (16 * NTW)), (unsigned)S, 1);
     if (mt == 2) dense_decode_wave_kernel<GATEUP, 2, NTW><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
     else dense_decode_wave_kernel<GATEUP, 1, NTW><<<grid, 64, 0, st>>>(A, W1, W3, rows, K, N, ksl, P);
