@@ -50,6 +50,21 @@ def test_parity_tiny_T(lib, T):
     check_case(_layer(inp, wl), inp, wl, path=PATH_DECODE)
 
 
+# widths that are odd multiples of 64: the decode kernels' 128-deep whole-line
+# batches leave single 32-deep steps, and the column tiles of both paths are
+# ragged (gate/up 192 of 256 columns, down 320 of 512)
+ODD = [(37, PATH_DECODE), (37, PATH_PREFILL), (300, PATH_PREFILL), (300, PATH_DECODE)]
+
+
+@pytest.mark.parametrize("T,path", ODD, ids=[f"T{c[0]}-p{c[1]}" for c in ODD])
+def test_parity_odd_widths(lib, T, path):
+    import dataclasses
+    wl = dataclasses.replace(workloads.get("dsmoe16b"), name="routed_odd", T=T, d=320, n_routed=16, d_ff=192,
+                             n_shared=1, top_k=4, family="rodd")
+    inp = gpu_inputs(wl, seed=6)
+    check_case(_layer(inp, wl), inp, wl, path=path)
+
+
 def test_full_size_skew512_sampled(lib):
     wl = workloads.get("skew512")
     inp = gpu_inputs(wl, seed=0)
