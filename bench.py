@@ -161,8 +161,8 @@ def main():
                     help="only run a plain device copy of MIB MiB (3 times): the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the layer runs on a single MI355X; see the sharding notes in the design document)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the layer runs on a single "
+              "MI355X (how it would shard across GPUs is described in the design document)", file=sys.stderr)
         sys.exit(2)
 
     import torch
