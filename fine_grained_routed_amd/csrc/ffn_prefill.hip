@@ -60,9 +60,6 @@
 #define PF_GM_SH 4   // m-tiles per ordering block (shared group)
 #define PF_LOADS 8   // DMA instructions per wave per operand per k-tile (8 rows of 128 B each)
 #define PF_NT 2      // cache-policy bits of a non-temporal load
-#ifndef PF_NT_ROWS
-#define PF_NT_ROWS 160  // routed rows per expert (mean) up to which the weights stream non-temporally
-#endif
 
 struct GemmArgs {
   const uint16_t *A;         // gate/up: u [T, d]; down: H [R, f]
@@ -76,7 +73,7 @@ struct GemmArgs {
   int64_t T;
   int64_t rows_a, rows_a_sh;  // rows of A and A_sh (bounds of their buffer resources)
   int E, K, K_sh, N, N_sh, has_shared;
-  int bnt;                   // routed weight tiles by non-temporal DMA (each weight line read by one tile)
+  int bnt;                   // single-m-tile experts' weights by non-temporal DMA
   int nt_r, nt_s;            // column tiles of a routed / the shared group
 };
 
@@ -449,7 +446,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
   // skips their DMA: nobody reads those LDS rows
   const bool adma = 64 * wvu < 32 * ns;
   // branch-free main loop per count of valid sub-tiles of this wave
-  if (a.bnt && !shared) {
+  // an expert with a single m-tile reads each of its weight lines once: those
+  // stream non-temporally (gate/up only; see launch_ffn_prefill_bf16)
+  if (a.bnt && !shared && mt_g == 1) {
     if (mw == 4) k_loop<4, PF_NT>(A, B, w, K, acc, adma);
     else if (mw == 3) k_loop<3, PF_NT>(A, B, w, K, acc, adma);
     else if (mw == 2) k_loop<2, PF_NT>(A, B, w, K, acc, adma);
@@ -567,11 +566,11 @@ hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u,
   g1.has_shared = hs;
   g1.nt_r = (f + PF_BN / 2 - 1) / (PF_BN / 2);
   g1.nt_s = hs ? (fs + PF_BN / 2 - 1) / (PF_BN / 2) : 1;
-  // with at most about one m-tile per expert, every routed gate/up weight line
-  // is read by a single tile: stream those weights non-temporally (DeepSeek-V3
-  // gate/up 8% faster at T = 512-1024, 5.5% at 2048, 1.7% at 4096; the down
-  // projection measured 4-6% slower this way from T = 1024 up and stays cached)
-  g1.bnt = E > 0 && R <= (int64_t)PF_NT_ROWS * E ? 1 : 0;
+  // routed experts with a single m-tile read each gate/up weight line once, so
+  // their tiles stream the weights non-temporally (DeepSeek-V3 gate/up 8%
+  // faster at T = 512-1024, 5.5% at 2048, 1.7% at 4096); the down projection
+  // measured 4-6% slower this way from T = 1024 up and stays cached
+  g1.bnt = E > 0 ? 1 : 0;
   const int64_t grid1 = pf_grid(mtile_bound(R, E) * g1.nt_r + mt_sh * g1.nt_s, PF_CHUNK_GU);
   grouped_gemm_bf16_kernel<true><<<dim3((unsigned)grid1), 256, 0, st>>>(g1);
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
