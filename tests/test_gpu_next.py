@@ -298,3 +298,42 @@ def test_group_limit_full_size_sampled(lib):
     wl = workloads.get("dsv3_prefill")
     inp = gpu_inputs(wl, seed=0)
     check_case(_layer(inp, wl, n_group=8, topk_group=4), inp, wl, sample=128)
+
+
+# --------------------------------------------- features combined on one layer
+COMBO = [("dsv3_prefill", 300, 8, 4, 0.75, PATH_PREFILL), ("dsv3_decode", None, 8, 4, 0.75, PATH_DECODE),
+         ("dsmoe16b", 517, 4, 1, 0.5, PATH_PREFILL), ("dsmoe16b", 40, 4, 1, 0.5, PATH_DECODE),
+         ("skew512", 333, 8, 2, 1.0, PATH_AUTO)]
+
+
+@pytest.mark.parametrize("name,T,ng,tg,cf,path", COMBO, ids=[f"{c[0]}-T{c[1]}-g{c[2]}x{c[3]}-cf{c[4]}-p{c[5]}"
+                                                               for c in COMBO])
+def test_capacity_with_group_limited_routing(lib, name, T, ng, tg, cf, path):
+    # the seat limit applies to the group-limited choice: grouping bit-exact,
+    # outputs to the layer tolerance, against the oracle's two rules composed
+    wl = workloads.get(name)
+    if T is not None:
+        wl = wl.with_T(T)
+    inp = gpu_inputs(wl, seed=7)
+    C = capacity_seats(cf, wl.T, wl.top_k, wl.n_routed)
+    r = check_case(_layer(inp, wl, capacity=C, n_group=ng, topk_group=tg), inp, wl, path=path)
+    log(f"[combo] {name} T={wl.T} C={C}: {r['dropped']} pairs dropped")
+
+
+@pytest.mark.parametrize("path", [PATH_PREFILL, PATH_DECODE])
+def test_block_with_capacity_and_group_limited_routing(lib, path):
+    # the pre-norm block around a layer with both limits equals x + that layer
+    # of the block's own normalisation, and that layer matches the oracle
+    wl = workloads.get("dsmoe16b").with_T(129)
+    binp = workloads.make_block_inputs(wl, seed=8, device="cuda")
+    C = capacity_seats(0.5, wl.T, wl.top_k, wl.n_routed)
+    layer = _layer(binp, wl, capacity=C, n_group=4, topk_group=2)
+    x, gamma = binp["x"], binp["gamma"]
+    out = layer.block_forward(x, gamma, EPS, path=path)
+    u = layer.rmsnorm(x, gamma, EPS)
+    lay = layer.forward(u, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(out, x.float() + lay)
+    inp = {k: v for k, v in binp.items() if k not in ("x", "gamma")}
+    inp["u"] = u
+    check_case(layer, inp, wl, path=path)
