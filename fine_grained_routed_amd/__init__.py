@@ -19,7 +19,6 @@ from ._binding import (  # noqa: F401
     MoeError,
     Options,
     Weights,
-    capacity_seats,
     load,
 )
-from .layer import MoELayer  # noqa: F401
+from .layer import MoELayer, capacity_seats  # noqa: F401

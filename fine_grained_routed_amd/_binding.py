@@ -186,14 +186,6 @@ class Library:
         return d.as_dict()
 
 
-def capacity_seats(capacity_factor, T: int, top_k: int, n_routed: int) -> int:
-    """Seats per expert for a capacity factor: ceil(cf * T * top_k / n_routed), in
-    exact rational arithmetic on the value of cf (a float counts as its binary value)."""
-    from fractions import Fraction
-    q = Fraction(capacity_factor) * T * top_k / n_routed
-    return -((-q.numerator) // q.denominator)
-
-
 _LOADED: Optional[Library] = None
 
 

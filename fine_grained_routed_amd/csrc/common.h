@@ -96,6 +96,9 @@ struct DiagWords {
 #define MOE_N_BM 5
 __host__ __device__ constexpr int moe_bm_of(int i) { return 16 << i; }  // 16 32 64 128 256
 
+// Tokens per call (keeps the per-token dispatches under 2^32 work-items).
+#define MOE_MAX_TOKENS (1 << 22)
+
 // Routing block: tokens per permutation work-group.
 #define MOE_PERM_BLOCK 256
 
@@ -255,6 +258,11 @@ hipError_t launch_ffn_decode(const moe_dims &dm, int64_t T, const void *u, const
                              const int32_t *counts, const int32_t *offsets, const int32_t *row_token,
                              float *y_rows, float *y_sh, const WsLayout &L, char *ws, hipStream_t st,
                              hipEvent_t ev_mid);
+// The largest 1-D grid, in work-groups of 256, that each expert-FFN launcher
+// would dispatch for T tokens (the host checks it before enqueueing).
+int64_t ffn_prefill_max_workgroups(const moe_dims &dm, int64_t T);
+int64_t ffn_decode_max_workgroups(const moe_dims &dm, int64_t T);
+int64_t ffn_f32_max_workgroups(const moe_dims &dm, int64_t T);
 // resid: NULL, or the block's raw input x [T, d] in dm.dtype, added last
 hipError_t launch_combine(const moe_dims &dm, int64_t T, const float *y_rows, const float *y_sh,
                           const float *topk_w, const int32_t *token_row, const void *resid, void *out,

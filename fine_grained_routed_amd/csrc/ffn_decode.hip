@@ -1,9 +1,9 @@
 // Decode path: expert FFNs for small token counts as HBM weight streaming.
 //
 // Source: "Shared and fine-grained experts", Developer level, 'Why not go finer
-// still': an expert processing a handful of tokens is a tiny GEMM that is
-// bound by loading its weights; Researcher level, Systems limits: grouped
-// kernels over many small experts.  "Shared Expert" (How it works): the
+// still' (with few tokens per expert, the expert GEMMs are small and their
+// time goes to reading weights from memory); Researcher level, Systems limits
+// (grouped kernels over many small experts).  "Shared Expert" (How it works): the
 // shared MLP runs on every token; here it is one more group.
 //
 // Work items are (16-row tile, column slice) pairs over the device-side tile
@@ -571,6 +571,40 @@ static hipError_t launch_dense_decode(const moe_dims &dm, int64_t T, const void 
 
 static int64_t dk_mtile_bound(int64_t R, int E) { return (R + DK_BM - 1) / DK_BM + std::min<int64_t>(E, R); }
 
+// Column width of a gate/up work-group: batches with few row tiles (the
+// smallest batches) take narrower column slices with deeper load batches,
+// which gives twice the work-groups (DeepSeek-V3 T=16: gate/up 0.89 ms
+// against 0.94).
+static bool dk_narrow(const moe_dims &dm, int64_t T) {
+  const int64_t R = T * dm.top_k;
+  return dk_mtile_bound(R, dm.n_routed) * ((dm.d_ff + dk_cols(DK_GU_NT) - 1) / dk_cols(DK_GU_NT)) < DK_NARROW_WGS;
+}
+
+// Work-groups of the routed layer's two launches.
+static void dk_grids(const moe_dims &dm, int64_t T, int64_t *grid1, int64_t *grid2) {
+  const int E = dm.n_routed, d = dm.d_model, f = dm.d_ff, fs = dm.d_ff_shared;
+  const int64_t R = T * dm.top_k;
+  const int64_t mt_sh = fs > 0 ? (T + DK_BM - 1) / DK_BM : 0;
+  const int c1 = dk_narrow(dm, T) ? dk_cols(1) : dk_cols(DK_GU_NT);
+  *grid1 = dk_mtile_bound(R, E) * ((f + c1 - 1) / c1) + mt_sh * (fs > 0 ? (fs + c1 - 1) / c1 : 1);
+  constexpr int c2 = dk_cols(DK_DN_NT);
+  *grid2 = (dk_mtile_bound(R, E) + mt_sh) * ((d + c2 - 1) / c2);
+}
+
+int64_t ffn_decode_max_workgroups(const moe_dims &dm, int64_t T) {
+  if (dm.n_routed == 0) {
+    // dense layer: passes of at most MOE_DD_ROWS rows; the pass kernels' 2-D/3-D
+    // grids are small in every dimension, the 1-D reduction of a pass with N
+    // output columns takes rows * N / 4 / 256 work-groups
+    const int64_t rows = std::min<int64_t>(T, MOE_DD_ROWS);
+    const int64_t n = std::max<int64_t>(dm.d_ff_shared, dm.d_model);
+    return (rows * n / 4 + 255) / 256;
+  }
+  int64_t g1, g2;
+  dk_grids(dm, T, &g1, &g2);
+  return std::max(g1, g2);
+}
+
 hipError_t launch_ffn_decode(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w,
                              const int32_t *counts, const int32_t *offsets, const int32_t *row_token,
                              float *y_rows, float *y_sh, const WsLayout &L, char *ws, hipStream_t st,
@@ -603,14 +637,12 @@ hipError_t launch_ffn_decode(const moe_dims &dm, int64_t T, const void *u, const
   g1.K_sh = d;
   g1.N = f;
   g1.N_sh = fs;
-  // few row tiles (the smallest batches): narrower column slices with deeper
-  // batches give twice the work-groups (DeepSeek-V3 T=16: gate/up 0.89 ms
-  // against 0.94)
-  const bool narrow = dk_mtile_bound(R, E) * ((f + dk_cols(DK_GU_NT) - 1) / dk_cols(DK_GU_NT)) < DK_NARROW_WGS;
+  const bool narrow = dk_narrow(dm, T);
   const int c1 = narrow ? dk_cols(1) : dk_cols(DK_GU_NT);
   g1.ns_r = (f + c1 - 1) / c1;
   g1.ns_s = hs ? (fs + c1 - 1) / c1 : 1;
-  const int64_t grid1 = dk_mtile_bound(R, E) * g1.ns_r + mt_sh * g1.ns_s;
+  int64_t grid1, grid2;
+  dk_grids(dm, T, &grid1, &grid2);
   if (narrow) decode_ffn_kernel<true, 1, 8><<<dim3((unsigned)grid1), 256, 0, st>>>(g1);
   else decode_ffn_kernel<true, DK_GU_NT, DK_GU_U><<<dim3((unsigned)grid1), 256, 0, st>>>(g1);
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
@@ -634,7 +666,6 @@ hipError_t launch_ffn_decode(const moe_dims &dm, int64_t T, const void *u, const
   constexpr int c2 = dk_cols(DK_DN_NT);
   g2.ns_r = (d + c2 - 1) / c2;
   g2.ns_s = g2.ns_r;
-  const int64_t grid2 = dk_mtile_bound(R, E) * g2.ns_r + mt_sh * g2.ns_s;
   decode_ffn_kernel<false, DK_DN_NT, DK_DN_U><<<dim3((unsigned)grid2), 256, 0, st>>>(g2);
   return hipGetLastError();
 }

@@ -138,6 +138,22 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgsF a) {
   }
 }
 
+// Work-groups of each launch below: 64-row tiles times column tiles.
+static void f32_grids(const moe_dims &dm, int64_t T, int64_t *grid1, int64_t *grid2) {
+  const int E = dm.n_routed, d = dm.d_model, f = dm.d_ff, fs = dm.d_ff_shared;
+  const int64_t R = T * dm.top_k;
+  const int64_t mtb = (R + F_BM - 1) / F_BM + std::min<int64_t>(E, R);
+  const int64_t mts = fs > 0 ? (T + F_BM - 1) / F_BM : 0;
+  *grid1 = mtb * ((f + F_BN / 2 - 1) / (F_BN / 2)) + mts * (fs > 0 ? (fs + F_BN / 2 - 1) / (F_BN / 2) : 1);
+  *grid2 = (mtb + mts) * ((d + F_BN - 1) / F_BN);
+}
+
+int64_t ffn_f32_max_workgroups(const moe_dims &dm, int64_t T) {
+  int64_t g1, g2;
+  f32_grids(dm, T, &g1, &g2);
+  return std::max(g1, g2);
+}
+
 hipError_t launch_ffn_f32(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w, const int32_t *offsets,
                           const int32_t *row_token, float *y_rows, float *y_sh, const WsLayout &L, char *ws,
                           hipStream_t st, hipEvent_t ev_mid) {
@@ -152,10 +168,12 @@ hipError_t launch_ffn_f32(const moe_dims &dm, int64_t T, const void *u, const mo
   GemmArgsF g1{(const float *)u, (const float *)u, row_token, offsets, tile_off, (const float *)w.w1,
                (const float *)w.w3, (const float *)w.w1s, (const float *)w.w3s, H, Hs, T, E, d, d, f, fs, hs,
                (f + F_BN / 2 - 1) / (F_BN / 2), hs ? (fs + F_BN / 2 - 1) / (F_BN / 2) : 1};
-  grouped_gemm_f32_kernel<true><<<dim3((unsigned)(mtb * g1.nt_r + mts * g1.nt_s)), 256, 0, st>>>(g1);
+  int64_t grid1, grid2;
+  f32_grids(dm, T, &grid1, &grid2);
+  grouped_gemm_f32_kernel<true><<<dim3((unsigned)grid1), 256, 0, st>>>(g1);
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
   GemmArgsF g2{H, Hs, nullptr, offsets, tile_off, (const float *)w.w2, nullptr, (const float *)w.w2s, nullptr,
                y_rows, y_sh, T, E, f, fs, d, d, hs, (d + F_BN - 1) / F_BN, (d + F_BN - 1) / F_BN};
-  grouped_gemm_f32_kernel<false><<<dim3((unsigned)(mtb * g2.nt_r + mts * g2.nt_s)), 256, 0, st>>>(g2);
+  grouped_gemm_f32_kernel<false><<<dim3((unsigned)grid2), 256, 0, st>>>(g2);
   return hipGetLastError();
 }

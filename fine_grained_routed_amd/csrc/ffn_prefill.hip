@@ -532,6 +532,23 @@ static int64_t pf_grid(int64_t tiles, int chunk) {
   return (tiles + round - 1) / round * round;
 }
 
+// Work-groups of the two launches below (the larger is checked on the host).
+static void pf_grids(const moe_dims &dm, int64_t T, int64_t *grid1, int64_t *grid2) {
+  const int E = dm.n_routed, d = dm.d_model, f = dm.d_ff, fs = dm.d_ff_shared;
+  const int64_t R = T * dm.top_k;
+  const int64_t mt_sh = fs > 0 ? (T + PF_BM - 1) / PF_BM : 0;
+  const int64_t nt1_r = (f + PF_BN / 2 - 1) / (PF_BN / 2), nt1_s = fs > 0 ? (fs + PF_BN / 2 - 1) / (PF_BN / 2) : 1;
+  const int64_t nt2 = (d + PF_BN - 1) / PF_BN;
+  *grid1 = pf_grid(mtile_bound(R, E) * nt1_r + mt_sh * nt1_s, PF_CHUNK_GU);
+  *grid2 = pf_grid(mtile_bound(R, E) * nt2 + mt_sh * nt2, PF_CHUNK_DN);
+}
+
+int64_t ffn_prefill_max_workgroups(const moe_dims &dm, int64_t T) {
+  int64_t g1, g2;
+  pf_grids(dm, T, &g1, &g2);
+  return std::max(g1, g2);
+}
+
 hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u, const moe_weights &w,
                                    const int32_t *offsets, const int32_t *row_token, float *y_rows, float *y_sh,
                                    const WsLayout &L, char *ws, hipStream_t st, hipEvent_t ev_mid) {
@@ -571,7 +588,8 @@ hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u,
   // faster at T = 512-1024, 5.5% at 2048, 1.7% at 4096); the down projection
   // measured 4-6% slower this way from T = 1024 up and stays cached
   g1.bnt = E > 0 ? 1 : 0;
-  const int64_t grid1 = pf_grid(mtile_bound(R, E) * g1.nt_r + mt_sh * g1.nt_s, PF_CHUNK_GU);
+  int64_t grid1, grid2;
+  pf_grids(dm, T, &grid1, &grid2);
   grouped_gemm_bf16_kernel<true><<<dim3((unsigned)grid1), 256, 0, st>>>(g1);
   if (ev_mid) (void)hipEventRecord(ev_mid, st);
 
@@ -597,7 +615,6 @@ hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u,
   g2.nt_r = (d + PF_BN - 1) / PF_BN;
   g2.nt_s = g2.nt_r;
   g2.bnt = 0;
-  const int64_t grid2 = pf_grid(mtile_bound(R, E) * g2.nt_r + mt_sh * g2.nt_s, PF_CHUNK_DN);
   grouped_gemm_bf16_kernel<false><<<dim3((unsigned)grid2), 256, 0, st>>>(g2);
   return hipGetLastError();
 }

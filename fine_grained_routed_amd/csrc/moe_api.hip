@@ -65,6 +65,12 @@ static moe_status check_dims(const moe_dims *dm, int64_t T) {
   if (dm->d_ff_shared % 64 || dm->d_ff_shared > 65536)
     return fail(MOE_ERR_UNSUPPORTED, "d_ff_shared must be a multiple of 64, <= 65536");
   if (T * (int64_t)dm->top_k >= (int64_t)1 << 31) return fail(MOE_ERR_UNSUPPORTED, "T * top_k >= 2^31");
+  // one work-group of 512 work-items per token in the combine, one wave per
+  // token in top-k and RMSNorm: with T <= 2^22 every such dispatch stays under
+  // the 2^32 work-items of the dispatch packet's grid size
+  if (T > MOE_MAX_TOKENS)
+    return fail(MOE_ERR_UNSUPPORTED, "T = %lld exceeds %d tokens per call; split the token batch", (long long)T,
+                MOE_MAX_TOKENS);
   return MOE_OK;
 }
 
@@ -158,16 +164,28 @@ static bool needs_tile_offsets(const moe_dims &dm, int64_t T, const moe_options 
 
 // The bf16 prefill GEMMs address their operands through buffer resources
 // with 32-bit byte offsets: every matrix they read must stay under 4 GiB.
+// The expert-FFN launches of the chosen path must each stay under 2^32
+// work-items (the dispatch packet's grid size).
 static moe_status check_path_limits(const moe_dims &dm, int64_t T, const moe_options *o) {
-  if (dm.dtype != MOE_BF16 || pick_path(dm, T, o) != 1) return MOE_OK;
-  const uint64_t lim = (uint64_t)1 << 32;
-  const uint64_t R = (uint64_t)T * dm.top_k;
-  if ((uint64_t)T * dm.d_model * 2 >= lim || R * dm.d_ff * 2 >= lim || (uint64_t)T * dm.d_ff_shared * 2 >= lim ||
-      (uint64_t)dm.d_ff * dm.d_model * 2 >= lim || (uint64_t)dm.d_ff_shared * dm.d_model * 2 >= lim)
+  const int path = pick_path(dm, T, o);
+  if (dm.dtype == MOE_BF16 && path == 1) {
+    const uint64_t lim = (uint64_t)1 << 32;
+    const uint64_t R = (uint64_t)T * dm.top_k;
+    if ((uint64_t)T * dm.d_model * 2 >= lim || R * dm.d_ff * 2 >= lim || (uint64_t)T * dm.d_ff_shared * 2 >= lim ||
+        (uint64_t)dm.d_ff * dm.d_model * 2 >= lim || (uint64_t)dm.d_ff_shared * dm.d_model * 2 >= lim)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "prefill path: u [T, d], the hidden activations [T*k, f] / [T, f_s] and each weight matrix must "
+                  "be under 4 GiB (T = %lld); split the token batch",
+                  (long long)T);
+  }
+  const int64_t wgs = dm.dtype == MOE_F32 ? ffn_f32_max_workgroups(dm, T)
+                      : path == 2         ? ffn_decode_max_workgroups(dm, T)
+                                          : ffn_prefill_max_workgroups(dm, T);
+  if (wgs * 256 >= ((int64_t)1 << 32))
     return fail(MOE_ERR_UNSUPPORTED,
-                "prefill path: u [T, d], the hidden activations [T*k, f] / [T, f_s] and each weight matrix must "
-                "be under 4 GiB (T = %lld); split the token batch",
-                (long long)T);
+                "expert FFN: a launch of %lld work-groups of 256 exceeds the 2^32 work-items of one dispatch "
+                "(T = %lld); split the token batch",
+                (long long)wgs, (long long)T);
   return MOE_OK;
 }
 

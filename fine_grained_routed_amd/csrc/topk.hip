@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
       const int E0 = __builtin_amdgcn_readfirstlane(top - 240);
       long long best[EXACT_LIMBS];
       long long cur[EXACT_LIMBS];
-      int wn = -1;
+      int exact_win = -1;
 #pragma unroll
       for (int q = 0; q < EXACT_LIMBS; ++q) best[q] = 0;
       for (unsigned rest = member; ; ) {  // ascending expert order
@@ -276,15 +276,15 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
         exact_key<BF16>(urow, w, bias, e, d, E0, cur, bad);
         // keys are wave sums: make their uniformity explicit before comparing
         int better = 0;
-        if (wn >= 0) better = exact_cmp(cur, best) > 0 ? 1 : 0;
+        if (exact_win >= 0) better = exact_cmp(cur, best) > 0 ? 1 : 0;
         better = __builtin_amdgcn_readfirstlane(better);
-        if (wn < 0 || better) {
-          wn = e;
+        if (exact_win < 0 || better) {
+          exact_win = e;
 #pragma unroll
           for (int q = 0; q < EXACT_LIMBS; ++q) best[q] = cur[q];
         }
       }
-      win = __builtin_amdgcn_readfirstlane(wn);
+      win = __builtin_amdgcn_readfirstlane(exact_win);
       if (lane == 0) atomicAdd(&diag->exact_keys, (unsigned)cnt);
       break;
     }

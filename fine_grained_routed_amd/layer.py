@@ -11,6 +11,17 @@ from ._binding import MOE_BF16, MOE_F32, PATH_AUTO, Library, load
 _DT = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}
 
 
+def capacity_seats(capacity_factor, T: int, top_k: int, n_routed: int) -> int:
+    """Caller-side sizing of the per-expert seat limit the library takes as an
+    integer: ceil(cf * T * top_k / n_routed), in exact rational arithmetic on
+    the value of cf (a float counts as its binary value).  "What is an
+    'expert', really?", glossary: capacity is a seat limit per expert, set as
+    a multiple of the even share of the batch's assignments."""
+    from fractions import Fraction
+    q = Fraction(capacity_factor) * T * top_k / n_routed
+    return -((-q.numerator) // q.denominator)
+
+
 class MoELayer:
     """One shared + routed MoE FFN layer (or a dense FFN layer) whose weights live on the GPU.
 

@@ -56,10 +56,13 @@
  * n_group <= 64, n_routed % n_group == 0, 1 <= topk_group <= n_group and
  * topk_group * (n_routed / n_group) >= top_k;
  * d_model and d_ff (and d_ff_shared when non-zero) multiples of 64;
- * 64 <= d_model <= 32768; T * top_k < 2^31.  On the bf16 prefill path every
- * matrix the expert GEMMs read (u, the [T*k, f] and [T, f_s] hidden
- * activations, each expert's weight matrix) must be under 4 GiB; larger token
- * batches are rejected with MOE_ERR_UNSUPPORTED and must be split.
+ * 64 <= d_model <= 32768; T <= 4194304 (2^22) and T * top_k < 2^31.  On the
+ * bf16 prefill path every matrix the expert GEMMs read (u, the [T*k, f] and
+ * [T, f_s] hidden activations, each expert's weight matrix) must be under
+ * 4 GiB.  On every path each kernel dispatch must stay under 2^32 work-items
+ * (the dispatch packet's 32-bit grid size); the expert-FFN launches of the
+ * chosen path are checked for this before anything is enqueued.  Token batches
+ * past these limits are rejected with MOE_ERR_UNSUPPORTED and must be split.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -30,19 +30,34 @@ def combinations(n_experts: int, top_k: int) -> int:
     return num // den
 
 
-def expert_budget(width: int, intermediate: int, routed: int, top_k: int, shared: int = 0) -> Tuple[int, int]:
-    """(total, active) expert weights of one MoE layer, biases ignored.
+def swiglu_matrix_shapes(d_model: int, d_ff: int) -> List[Tuple[str, int, int]]:
+    """(name, rows, columns) of the three matrices one SwiGLU expert holds: the
+    gate and up projections map the d_model-wide token to d_ff, the down
+    projection maps back ("Shared Expert", How it works: FFN(u) = W2 (SiLU(W1 u)
+    * W3 u), with W1, W3 of shape d_ff x d_model and W2 of shape d_model x d_ff)."""
+    return [("gate", d_ff, d_model), ("up", d_ff, d_model), ("down", d_model, d_ff)]
 
-    Chinese page on fine-grained and shared experts, section on making the
-    budget equal: a SwiGLU expert holds three d x f matrices (gate, up, down),
-    i.e. 3*d*f weights and as many MACs per token; the shared experts count in
-    both the stored and the active totals.  Invalid configurations are
-    rejected.
+
+def expert_budget(d_model: int, d_ff: int, n_routed: int, top_k: int, n_shared: int = 0) -> Tuple[int, int]:
+    """(stored, active) expert weights of one MoE layer (biases ignored).
+
+    MoE page in Chinese on fine-grained and shared experts, the section that
+    equalises the budget: the stored count covers every routed and shared
+    expert, the active count per token covers the top_k routed experts the
+    router picks plus the always-on shared ones.  One expert's size is the
+    sum of its matrices' element counts.  Shapes that cannot describe a layer
+    raise ValueError.
     """
-    if min(width, intermediate, routed, top_k) < 1 or shared < 0 or top_k > routed:
-        raise ValueError("invalid expert configuration")
-    per_expert = 3 * width * intermediate
-    return per_expert * (routed + shared), per_expert * (top_k + shared)
+    if d_model < 1 or d_ff < 1:
+        raise ValueError(f"expert matrices need positive sizes, got d_model={d_model}, d_ff={d_ff}")
+    if n_routed < 1 or not 1 <= top_k <= n_routed:
+        raise ValueError(f"need 1 <= top_k <= n_routed, got top_k={top_k}, n_routed={n_routed}")
+    if n_shared < 0:
+        raise ValueError(f"n_shared must be >= 0, got {n_shared}")
+    size = sum(rows * cols for _, rows, cols in swiglu_matrix_shapes(d_model, d_ff))
+    held = {"routed": n_routed, "shared": n_shared}
+    used = {"routed": top_k, "shared": n_shared}
+    return size * sum(held.values()), size * sum(used.values())
 
 
 def layer_accounting(d_model: int, d_ff: int, n_routed: int, n_shared: int, top_k: int) -> dict:

@@ -9,8 +9,8 @@ HIP path.
   level in the official graph, while MoE.forward returns shared + routed only;
   Watch-outs -- the shared experts sit behind the FFN pre-norm too).
 * The dense prefix layers: "Shared and fine-grained experts" (Developer
-  level, after the table of configs: the first three DeepSeek-V3 layers keep
-  an ordinary dense feed-forward block of width 18432) and "Shared Expert"
+  level, after the table of configs: DeepSeek-V3's first three layers have no
+  experts, and their feed-forward block is a plain SwiGLU 18432 wide) and "Shared Expert"
   (Official code: the MLP class is the same SwiGLU as a dense prefix layer).
 
 Readings taken where the pages are silent (each also listed in the design

@@ -84,6 +84,31 @@ def test_negative_T_and_huge_T(lib):
     assert ei.value.status == B.MOE_ERR_UNSUPPORTED
 
 
+def test_token_cap(lib):
+    # every per-token dispatch (combine: 512 work-items a token) stays under
+    # the 2^32 work-items of one dispatch packet
+    d = _dims(lib, top_k=1)
+    assert lib.workspace_size(d, 1 << 22) > 0
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.workspace_size(d, (1 << 22) + 1)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED and "tokens per call" in str(ei.value)
+
+
+@pytest.mark.parametrize("kw,T,path", [
+    # fp32 GEMM: (2^26 / 64 row tiles) x (65536 / 32 column tiles) work-groups
+    (dict(d_model=64, n_routed=16, d_ff=65536, d_ff_shared=0, top_k=16, dtype=fgr.MOE_F32), 1 << 22, 0),
+    # forced decode path: (2^25 / 16 row tiles) x 16 column slices
+    (dict(d_model=7168, n_routed=256, d_ff=2048, d_ff_shared=2048, top_k=8), 1 << 22, 2),
+])
+def test_expert_ffn_grid_limit(lib, kw, T, path):
+    # rejected on the host before anything is enqueued (the pointers are never used)
+    d = _dims(lib, **kw)
+    w = _full_weights(lib, shared=kw["d_ff_shared"] > 0)
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.layer_forward(d, T, FAKE, w, FAKE, lib.options(path), FAKE, ws_bytes=1 << 62, stream=0)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED and "work-items" in str(ei.value)
+
+
 def test_workspace_size_grows_with_T(lib):
     d = _dims(lib)
     assert lib.workspace_size(d, 0) > 0

@@ -1,0 +1,124 @@
+"""GPU test of the routing certification under heavy cancellation.
+
+The router's first-level bound assumes that the matrix cores add each chunk of
+64 bf16 x bf16 products in fp32 with at most 2^-22 relative error per addition
+(any order).  These inputs make every 64-product chunk of every logit carry
+large products that cancel exactly (the chunk's exact sum is 0), so the fp32
+partial sums are large and lose low bits, while the exact logits are set by a
+separate block of carrier coordinates.  For each token, the exact gap between
+its k-th and (k+1)-th logits is placed at a chosen multiple of the two logits'
+first-level bounds: below 1 the first level cannot settle the comparison and
+the fp64 level must; at 2 the first level settles it by itself, which is only
+right if the hardware's rounding stays inside the bound; a zero gap (an exact
+tie) needs the exact level and goes to the lower index.  Routing must match
+the oracle bit for bit on every token, and the diagnostics must show the
+refinement levels at work.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from fine_grained_routed_amd import MoELayer
+from tests.parity import check_case, gpu_inputs, log
+
+pytestmark = pytest.mark.gpu
+
+RATIOS = (0.5, 1.0, 2.0)
+
+
+def _bf16(x: np.ndarray) -> np.ndarray:
+    """Round to bf16 values (as fp64) through torch's conversion."""
+    return torch.from_numpy(x).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _level1_bound(u_row: np.ndarray, c: np.ndarray, logit: np.ndarray, d: int) -> np.ndarray:
+    """First-level bound of each expert's logit for one token, as the router
+    states it: (64 * 2^-22 + (d / 64 + 2) * 2^-52) * ||u|| ||c_e|| (1 + 2^-30)
+    + 2^-50 |L| + d * 2^-120."""
+    c1 = 64 * 2.0 ** -22 + (d / 64 + 2) * 2.0 ** -52
+    return (c1 * np.linalg.norm(u_row) * np.linalg.norm(c, axis=1) * (1 + 2.0 ** -30)
+            + 2.0 ** -50 * np.abs(logit) + d * 2.0 ** -120)
+
+
+def _cancelling_inputs(E: int, k: int, d: int, per_ratio: int, ties: int, seed: int):
+    """u [T, d] and router [E, d] as bf16-exact fp64 arrays, the exact logits
+    [T, E], and each token's target ratio (0 for an exact tie)."""
+    rng = np.random.default_rng([seed, E, k, d])
+    ncar = (E + 63) // 64 * 64           # carrier coordinates: the last ncar of d
+    nch = (d - ncar) // 64               # cancelling chunks before them
+    ratios = [r for r in RATIOS for _ in range(per_ratio)] + [0.0] * ties
+    T = len(ratios)
+
+    def wide(shape):  # bf16 values with 8 significant bits and exponents -4..4, random signs
+        m = rng.integers(128, 256, size=shape) / 128.0
+        return rng.choice([-1.0, 1.0], size=shape) * m * np.exp2(rng.integers(-4, 5, size=shape))
+
+    u = np.zeros((T, d))
+    c = np.zeros((E, d))
+    for ch in range(nch):
+        x, y = wide((T, 32)), wide((E, 32))
+        lo = 64 * ch
+        # positions lo..lo+31 hold x . y, positions lo+32..lo+63 hold x . (-y):
+        # every chunk's exact sum is 0, its partial sums are not
+        u[:, lo:lo + 32] = x
+        u[:, lo + 32:lo + 64] = x
+        c[:, lo:lo + 32] = y
+        c[:, lo + 32:lo + 64] = -y
+    c[np.arange(E), d - ncar + np.arange(E)] = 1.0   # expert e's exact logit is u[t, d - ncar + e]
+
+    for t, ratio in enumerate(ratios):
+        order = rng.permutation(E)      # order[r] is the expert meant for rank r
+        v = np.zeros(E)
+        for it in range(8):             # the carriers enter ||u||: iterate to the fixed point
+            u[t, d - ncar:d - ncar + E] = v
+            B = _level1_bound(u[t], c, v, d)
+            bm = B.max()
+            # ranks above k: 3 bounds apart; below k + 1: 8 bounds down (all equal);
+            # the carriers stay small against the cancelling part's norm
+            v = np.full(E, -8.0 * bm)
+            for r in range(k - 1):
+                v[order[r]] = 3.0 * bm * (k - 1 - r)
+            a, b = order[k - 1], order[k]   # ranks k and k+1
+            v[a] = 0.0
+            v[b] = -ratio * (B[a] + B[b])
+            v = _bf16(v)
+        u[t, d - ncar:d - ncar + E] = v
+    exact = u[:, d - ncar:d - ncar + E].copy()
+    assert np.array_equal(_bf16(u), u) and np.array_equal(_bf16(c), c)
+    return u, c, exact, np.array(ratios)
+
+
+@pytest.mark.parametrize("E,k,d,per_ratio,ties", [
+    (8, 2, 512, 40, 8),       # few tokens: the router's split-K path
+    (256, 8, 1024, 1400, 100),  # 4300 tokens x 256 experts: one reduction slice
+], ids=["E8k2_splitk", "E256k8"])
+def test_certification_under_cancellation(lib, E, k, d, per_ratio, ties):
+    u, c, exact, ratios = _cancelling_inputs(E, k, d, per_ratio, ties, seed=11)
+    T = u.shape[0]
+    # the placed gaps, measured against the bound of the exact logits
+    srt = -np.sort(-exact, axis=1)
+    gap = srt[:, k - 1] - srt[:, k]
+    for t in range(T):
+        B = _level1_bound(u[t], c, exact[t], d)
+        top = np.argsort(-exact[t], kind="stable")
+        got = gap[t] / (B[top[k - 1]] + B[top[k]])
+        assert abs(got - ratios[t]) <= 0.01 * max(ratios[t], 1.0), (t, got, ratios[t])
+    wl = workloads.Workload("certify", T, d, E, 64, 1, k, "bf16", None, f"certify{E}", "cancellation")
+    inp = gpu_inputs(wl, seed=12)
+    inp["u"] = torch.from_numpy(u).to(torch.float32).to(torch.bfloat16).cuda()
+    inp["w_router"] = torch.from_numpy(c).to(torch.float32).to(torch.bfloat16).cuda()
+    layer = MoELayer({kk: vv for kk, vv in inp.items() if kk != "u"}, k)
+    r = check_case(layer, inp, wl, sample=min(T, 1024))
+    diag = r["diag"]
+    log(f"[certify] E={E} T={T}: diagnostics {diag}")
+    # every gap below the bound and every tie needs refinement; ties need exact keys
+    n_open = int(((ratios > 0) & (ratios < 1)).sum()) + ties
+    assert diag["tokens_exact"] >= n_open
+    assert diag["refinements"] >= n_open
+    assert diag["exact_keys"] >= 2 * ties
+    # exact ties go to the lower expert index
+    idx = layer.router_topk(inp["u"])[0].cpu().numpy()
+    for t in np.nonzero(ratios == 0.0)[0]:
+        tied = np.nonzero(exact[t] == srt[t, k - 1])[0]
+        assert idx[t, k - 1] == tied.min()

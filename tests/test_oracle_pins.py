@@ -59,7 +59,7 @@ def test_equal_budget_identity():
     res = [acc.expert_budget(g["d"], c["intermediate"], c["routed"], c["top_k"], c["shared"])
            for c in (g["coarse"], g["fine"], g["with_shared"])]
     assert res[0] == res[1] == res[2] == tuple(g["expected"])
-    assert 3 * g["d"] * 256 == g["per_expert_f256"]
+    assert sum(r * c for _, r, c in acc.swiglu_matrix_shapes(g["d"], 256)) == g["per_expert_f256"]
     e = g["eight_plus_shared"]
     _, active = acc.expert_budget(g["d"], e["intermediate"], e["routed"], e["top_k"], e["shared"])
     assert active == e["active"]
