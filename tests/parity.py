@@ -84,7 +84,8 @@ def oracle_outputs(u64, toks, a, k, idx_o, token_row_o, capacity, groups=(None, 
             oracle.combine(r["y_rows"], None, gates, r["token_row"]))
 
 
-def check_case(layer, inp, wl: workloads.Workload, path: int = 0, sample: Optional[int] = None, seed: int = 0):
+def check_case(layer, inp, wl: workloads.Workload, path: int = 0, sample: Optional[int] = None, seed: int = 0,
+               gate_tol: float = GATE_TOL):
     """Full parity check of one case.  sample=None compares every token's output;
     otherwise routing is compared on all tokens and outputs on a seeded sample.
     A layer built with a capacity is checked against the oracle's capacity rule."""
@@ -103,7 +104,7 @@ def check_case(layer, inp, wl: workloads.Workload, path: int = 0, sample: Option
     assert bad.size == 0, (f"top-k differs on {bad.size} tokens, first {bad[:5]}: gpu {idx_g[bad[:3]]} "
                            f"oracle {idx_o[bad[:3]]}; diagnostics {g['diag']}")
     gerr = float(np.max(np.abs(g["gw"].cpu().numpy().astype(np.float64) - gw_o)))
-    assert gerr <= GATE_TOL, f"gate error {gerr}"
+    assert gerr <= gate_tol, f"gate error {gerr} > {gate_tol}"
     counts_o, offsets_o, row_token_o, token_row_o = oracle.permute(idx_o, wl.n_routed, cap)
     assert np.array_equal(g["counts"].cpu().numpy(), counts_o)
     assert np.array_equal(g["offsets"].cpu().numpy(), offsets_o)

@@ -109,7 +109,12 @@ def test_certification_under_cancellation(lib, E, k, d, per_ratio, ties):
     inp["u"] = torch.from_numpy(u).to(torch.float32).to(torch.bfloat16).cuda()
     inp["w_router"] = torch.from_numpy(c).to(torch.float32).to(torch.bfloat16).cuda()
     layer = MoELayer({kk: vv for kk, vv in inp.items() if kk != "u"}, k)
-    r = check_case(layer, inp, wl, sample=min(T, 1024))
+    # The kept gates are softmax values of the router's computed logits, whose
+    # rounding these inputs make deliberately large (fp32 chunk partial sums
+    # near 3e3, an ulp of 2^-12, against logits of order 1), so they are held
+    # to 1e-3 here instead of 1e-5; a renormalised or misplaced gate is off by
+    # 0.1 or more.  Routing and outputs keep their usual bounds.
+    r = check_case(layer, inp, wl, sample=min(T, 1024), gate_tol=1e-3)
     diag = r["diag"]
     log(f"[certify] E={E} T={T}: diagnostics {diag}")
     # every gap below the bound and every tie needs refinement; ties need exact keys
