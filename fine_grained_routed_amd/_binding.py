@@ -21,7 +21,9 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_VALUE", 2: "MOE_ERR_UNSUPPORTED
 
 # the functions include/moe.h declares
 EXPORTS = ("moe_workspace_size", "moe_router_topk", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_layer_forward", "moe_rmsnorm", "moe_block_forward", "moe_read_diagnostics", "moe_last_error")
+           "moe_layer_forward", "moe_layer_forward_static", "moe_rmsnorm", "moe_block_forward",
+           "moe_read_diagnostics", "moe_last_error")
+STATIC_WS_BYTES = 64 << 20  # MOE_STATIC_WS_BYTES
 
 
 class MoeError(RuntimeError):
@@ -66,6 +68,8 @@ _SIG = {
     "moe_combine": [ctypes.POINTER(Dims), _I64, _P, _P, _P, _P, _P, _P],
     "moe_layer_forward": [ctypes.POINTER(Dims), _I64, _P, ctypes.POINTER(Weights), _P, ctypes.POINTER(Options), _P,
                           ctypes.c_size_t, _P],
+    "moe_layer_forward_static": [ctypes.POINTER(Dims), _I64, _P, ctypes.POINTER(Weights), _P,
+                                 ctypes.POINTER(Options), _P],
     "moe_rmsnorm": [ctypes.POINTER(Dims), _I64, _P, _P, ctypes.c_double, _P, _P],
     "moe_block_forward": [ctypes.POINTER(Dims), _I64, _P, _P, ctypes.c_double, ctypes.POINTER(Weights), _P,
                           ctypes.POINTER(Options), _P, ctypes.c_size_t, _P],
@@ -167,6 +171,11 @@ class Library:
                                                None if options is None else ctypes.byref(options), _ptr(ws),
                                                ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes,
                                                _stream(stream)))
+
+    def layer_forward_static(self, dims, T, u, weights: Weights, out, options: Optional[Options], stream=None):
+        self._check(self.lib.moe_layer_forward_static(ctypes.byref(dims), T, _ptr(u), ctypes.byref(weights),
+                                                      _ptr(out), None if options is None else ctypes.byref(options),
+                                                      _stream(stream)))
 
     def rmsnorm(self, dims, T, x, norm_weight, eps, u, stream=None):
         self._check(self.lib.moe_rmsnorm(ctypes.byref(dims), T, _ptr(x), _ptr(norm_weight), float(eps), _ptr(u),

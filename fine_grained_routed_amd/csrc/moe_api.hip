@@ -6,6 +6,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "common.h"
 
 static thread_local char g_err[512] = "";
@@ -265,6 +267,37 @@ static moe_status run_layer(const moe_dims &dm, int64_t T, const void *u, const 
   return MOE_OK;
 }
 
+// ------------------------------------------------ library-owned scratch memory
+// moe_layer_forward_static's workspace: one array per device, allocated with
+// the code object when the library is first used on that device and held
+// until the process ends.  In host code `scratch` names a host-side stand-in
+// of the array, not its device address; the device address is looked up once
+// per device (with that device current) and only that address is handed to
+// kernels.
+static __device__ __align__(256) char scratch[MOE_STATIC_WS_BYTES];
+
+#define MOE_MAX_DEVICES 64
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[MOE_MAX_DEVICES];
+
+// Device address of the current device's scratch array (looked up on first use).
+static moe_status scratch_for_current_device(char **out) {
+  int dev = -1;
+  MOE_TRY_HIP(hipGetDevice(&dev), "static scratch: hipGetDevice");
+  if (dev < 0 || dev >= MOE_MAX_DEVICES)
+    return fail(MOE_ERR_UNSUPPORTED, "static scratch: device %d is beyond the %d devices supported", dev,
+                MOE_MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    MOE_TRY_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "static scratch: hipGetSymbolAddress");
+    if (!p) return fail(MOE_ERR_HIP, "static scratch: hipGetSymbolAddress returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (char *)g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 extern "C" {
 
 const char *moe_last_error(void) { return g_err; }
@@ -385,6 +418,29 @@ moe_status moe_layer_forward(const moe_dims *dims, int64_t T, const void *u, con
   EventHook ev{opts, st};
   ev.rec(0);
   return run_layer(*dims, T, u, *wts, nullptr, out, opts, L, (char *)ws, st, ev);
+}
+
+moe_status moe_layer_forward_static(const moe_dims *dims, int64_t T, const void *u, const moe_weights *wts,
+                                    void *out, const moe_options *opts, void *stream) {
+  MOE_CHECK(check_dims(dims, T));
+  MOE_CHECK(check_opts(opts));
+  if (T == 0) return MOE_OK;
+  MOE_CHECK(check_ptr(u, "u"));
+  MOE_CHECK(check_weights(*dims, wts, true, true));
+  MOE_CHECK(check_ptr(out, "out"));
+  const WsLayout L = moe_ws_layout(*dims, T);
+  if (L.total > (size_t)MOE_STATIC_WS_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "static scratch: this call needs %zu bytes of workspace, the library's scratch holds %zu; "
+                "use moe_layer_forward with a workspace or split the token batch",
+                L.total, (size_t)MOE_STATIC_WS_BYTES);
+  MOE_CHECK(check_path_limits(*dims, T, opts));
+  char *w = nullptr;
+  MOE_CHECK(scratch_for_current_device(&w));
+  hipStream_t st = (hipStream_t)stream;
+  EventHook ev{opts, st};
+  ev.rec(0);
+  return run_layer(*dims, T, u, *wts, nullptr, out, opts, L, w, st, ev);
 }
 
 moe_status moe_rmsnorm(const moe_dims *dims, int64_t T, const void *x, const float *norm_weight, double eps, void *u,

@@ -207,6 +207,28 @@ moe_status moe_layer_forward(const moe_dims *dims, int64_t T, const void *u, con
                              void *out, const moe_options *opts, void *ws, size_t ws_bytes,
                              void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as moe_layer_forward, computing the same result bit for bit, with the
+ * workspace taken from a library-owned device array of MOE_STATIC_WS_BYTES
+ * (64 MiB) instead of a `ws` argument.  The caller still passes u, the
+ * weights and out.  Nothing is allocated or freed by the call: the array is
+ * part of the library's code object, one per device, held by each device the
+ * library runs on until the process ends; its device address is looked up
+ * once per device on the first call made with that device current (the
+ * current device must be the one `stream` belongs to).  A call whose
+ * workspace (moe_workspace_size) exceeds MOE_STATIC_WS_BYTES is rejected with
+ * MOE_ERR_WORKSPACE before anything is enqueued; at the DeepSeek-V3 shape this
+ * covers decode batches (T = 64 needs about 27 MB).  Every call on one device
+ * shares that device's array and leaves its contents behind for the next:
+ * calls that overlap on one device (two streams, two threads) race and must
+ * be serialised by the caller.  Intermediates that must start cleared are
+ * cleared by the call's own kernels, so no call depends on what the previous
+ * one left. */
+#define MOE_STATIC_WS_BYTES (64 << 20)
+moe_status moe_layer_forward_static(const moe_dims *dims, int64_t T, const void *u, const moe_weights *w,
+                                    void *out, const moe_options *opts, void *stream);
+
 /* RMSNorm of the residual stream: u[t,:] = x[t,:] / sqrt(mean_c x[t,c]^2 + eps) * norm_weight[:].
  * x and u are [T, d_model] in dims->dtype; norm_weight [d_model] is fp32.
  * The mean of squares, the scale and the products are evaluated in fp64 and

@@ -109,6 +109,17 @@ def test_expert_ffn_grid_limit(lib, kw, T, path):
     assert ei.value.status == B.MOE_ERR_UNSUPPORTED and "work-items" in str(ei.value)
 
 
+def test_static_scratch_rejects_a_large_call(lib):
+    # a call whose workspace exceeds the library's 64 MiB scratch is refused on
+    # the host, before the scratch is looked up or anything is enqueued
+    d = _dims(lib, d_model=7168, n_routed=256, d_ff=2048, d_ff_shared=2048, top_k=8)
+    assert lib.workspace_size(d, 16384) > B.STATIC_WS_BYTES
+    with pytest.raises(fgr.MoeError) as ei:
+        lib.layer_forward_static(d, 16384, FAKE, _full_weights(lib), FAKE, None, stream=0)
+    assert ei.value.status == B.MOE_ERR_WORKSPACE and "scratch" in str(ei.value)
+    lib.layer_forward_static(d, 0, None, lib.weights(), None, None, stream=0)  # T = 0: no-op
+
+
 def test_workspace_size_grows_with_T(lib):
     d = _dims(lib)
     assert lib.workspace_size(d, 0) > 0
