@@ -324,6 +324,29 @@ __device__ __forceinline__ void k_loop(const Operand &A, const Operand &B, const
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
+// Sixteen 16-byte LDS reads at addr + off[k] issued back to back, then one
+// wait: the epilogue's read-backs travel together instead of one LDS round
+// trip per output store (the compiler would otherwise place each read next to
+// its store).  The wait is inside the same statement, so no result register
+// is used or reused before its read has landed.
+#define PF_LDS16_OFFS(S, B) "i"((B) + 0 * (S)), "i"((B) + 1 * (S)), "i"((B) + 2 * (S)), "i"((B) + 3 * (S))
+#define PF_LDS_READ16(v, addr, SI, SJ)                                                                         \
+  asm volatile(                                                                                              \
+      "ds_read_b128 %0, %16 offset:%17\n\tds_read_b128 %1, %16 offset:%18\n\t"                           \
+      "ds_read_b128 %2, %16 offset:%19\n\tds_read_b128 %3, %16 offset:%20\n\t"                           \
+      "ds_read_b128 %4, %16 offset:%21\n\tds_read_b128 %5, %16 offset:%22\n\t"                           \
+      "ds_read_b128 %6, %16 offset:%23\n\tds_read_b128 %7, %16 offset:%24\n\t"                           \
+      "ds_read_b128 %8, %16 offset:%25\n\tds_read_b128 %9, %16 offset:%26\n\t"                           \
+      "ds_read_b128 %10, %16 offset:%27\n\tds_read_b128 %11, %16 offset:%28\n\t"                         \
+      "ds_read_b128 %12, %16 offset:%29\n\tds_read_b128 %13, %16 offset:%30\n\t"                         \
+      "ds_read_b128 %14, %16 offset:%31\n\tds_read_b128 %15, %16 offset:%32\n\t"                         \
+      "s_waitcnt lgkmcnt(0)"                                                                                 \
+      : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(v[4]), "=v"(v[5]), "=v"(v[6]), "=v"(v[7]),      \
+        "=v"(v[8]), "=v"(v[9]), "=v"(v[10]), "=v"(v[11]), "=v"(v[12]), "=v"(v[13]), "=v"(v[14]), "=v"(v[15]) \
+      : "v"(addr), PF_LDS16_OFFS(SJ, 0), PF_LDS16_OFFS(SJ, SI), PF_LDS16_OFFS(SJ, 2 * (SI)),                 \
+        PF_LDS16_OFFS(SJ, 3 * (SI))                                                                          \
+      : "memory")
+
 template <bool GATEUP>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -469,33 +492,48 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
   // sub-tile at a time (rows padded by 16 bytes), and leaves as whole 512-byte
   // rows; the smaller bf16 output is stored directly.  First every wave's DMA
   // has landed and every fragment read is done, so all stages are free.
-  if (!GATEUP) __syncthreads();
+  publish<0>();  // every wave's DMA has landed and every fragment read is done: all stages are free
   char *stg = (char *)(wv == 0 ? g_As0 : wv == 1 ? g_Bs0 : wv == 2 ? g_Bs1 : g_Bs2);
   const int mrow = lane & 31;
   const int cgrp = 4 * (lane >> 5);
   if (GATEUP) {
-    // H: each lane stores its four consecutive bf16 columns directly
+    // H: the wave's 64 bf16 columns (j = 0, 1) of each 32-row sub-tile, one
+    // 128-byte line per row, turned around in the wave's stage and stored 8
+    // rows per instruction
+    constexpr int RS = 144;
     uint16_t *C = (uint16_t *)(shared ? a.C_sh : a.C);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int nb = nt * (PF_BN / 2) + wn * 64 + j * 32 + cgrp;
-      if (nb >= N) continue;  // N is a multiple of 64: a group of 4 is all in or all out
+    const int nb = nt * (PF_BN / 2) + wn * 64;
+    if (nb < N) {  // N is a multiple of 64: the wave's 64 columns are all in or all out
 #pragma unroll
       for (int i = 0; i < PF_WM; ++i) {
-        const int row = w.a0 + i * 32 + mrow;
-        if (i >= mw || row >= valid) continue;
-        uint16_t *crow = C + (rb + row) * (int64_t)N + nb;
+        if (i >= mw) continue;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float h[4];
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) h[c] = silu_fast(acc[i][j][4 * q + c]) * acc[i][j + 2][4 * q + c];
-          *(uint2 *)(crow + 8 * q) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-        }
+          for (int q = 0; q < 4; ++q) {
+            float h[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) h[c] = silu_fast(acc[i][j][4 * q + c]) * acc[i][j + 2][4 * q + c];
+            *(uint2 *)(stg + (i * 32 + mrow) * RS + (32 * j + 8 * q + cgrp) * 2) =
+                make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+          }
       }
+      __builtin_amdgcn_wave_barrier();
+      // read-back k = 4 i + sg: rows 8 sg + lane / 8 of sub-tile i (past the
+      // valid sub-tiles it reads unused rows of the stage, never stored)
+      uint4 v[16];
+      PF_LDS_READ16(v, (uint32_t)(uintptr_t)(stg + (lane >> 3) * RS + (lane & 7) * 16), 32 * RS, 8 * RS);
+#pragma unroll
+      for (int i = 0; i < PF_WM; ++i)
+#pragma unroll
+        for (int sg = 0; sg < 4; ++sg) {
+          const int row = w.a0 + i * 32 + 8 * sg + (lane >> 3);
+          if (i < mw && row < valid) *(uint4 *)(C + (rb + row) * (int64_t)N + nb + (lane & 7) * 8) = v[4 * i + sg];
+        }
     }
   } else {
-    // Y: 128 fp32 columns (512 bytes) per row of the wave
+    // Y: 128 fp32 columns (512 bytes) per row of the wave; all 16 read-backs
+    // of a sub-tile are issued before its stores
     constexpr int RS = 528;
     float *C = (float *)(shared ? a.C_sh : a.C);
     const int nb = nt * PF_BN + wn * 128;
@@ -510,12 +548,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
               make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
       __builtin_amdgcn_wave_barrier();
       const int col = nb + (lane & 31) * 4;  // 32 lanes per 512-byte row
+      // read-back t: rows 2 t + lane / 32
+      uint4 v[16];
+      PF_LDS_READ16(v, (uint32_t)(uintptr_t)(stg + (lane >> 5) * RS + (lane & 31) * 16), 8 * RS, 2 * RS);
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const int r = (lane >> 5) + 2 * t;
-        const float4 v = *(const float4 *)(stg + r * RS + (lane & 31) * 16);
-        const int row = w.a0 + i * 32 + r;
-        if (col < N && row < valid) *(float4 *)(C + (rb + row) * (int64_t)N + col) = v;
+        const int row = w.a0 + i * 32 + (lane >> 5) + 2 * t;
+        if (col < N && row < valid) *(uint4 *)(C + (rb + row) * (int64_t)N + col) = v[t];
       }
       __builtin_amdgcn_wave_barrier();
     }
