@@ -47,6 +47,45 @@ __device__ __forceinline__ uint4 keep_or_zero(bool ok, uint4 v) {
   return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
 }
 
+// ------------------------------------------------- direct-to-LDS DMA helpers
+// (used by the tiled matrix-core kernels: the prefill grouped GEMMs and the
+// router logits)
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// LDS rows of 64 bf16 hold eight 16-byte chunks; chunk c of row r sits in slot
+// c ^ swz(r).  swz is one-to-one on any 8 consecutive rows and on any 8 rows
+// of one parity among 16 consecutive rows, so the 16-byte fragment reads of 8
+// (or 16) consecutive rows fall on distinct banks whether the LDS serves 8
+// lanes over 32 banks or 16 lanes over 64 banks per cycle.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// Buffer resource over `bytes` bytes at `base` (raw buffer: no stride, 32-bit
+// data format), the form the buffer-to-LDS loads address memory through.
+// Accesses past `bytes` read zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                           (int)(uint32_t)min(bytes, (uint64_t)0xffffffffu), 0x00020000);
+}
+
+// s_waitcnt immediate (gfx9 layout: vmcnt [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]) for "at most vm vector-memory operations outstanding, LDS
+// and scalar loads complete".  The builtin, unlike inline asm, is visible to
+// the compiler's own wait tracking, which then knows that older DMA into a
+// stage has landed.
+constexpr int waitcnt_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4); }
+
+// Publish LDS to the work-group: this wave's LDS reads are complete and at
+// most `vm` DMA instructions are still in flight, then the work-group barrier.
+// Written out rather than __syncthreads(), whose release fence would also
+// wait for every DMA in flight and so drain the prefetch.
+template <int VM>
+__device__ __forceinline__ void publish() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------ wave reductions
 __device__ __forceinline__ double wave_max_f64(double v) {
 #pragma unroll

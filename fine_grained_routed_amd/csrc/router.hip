@@ -170,6 +170,252 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const uint16_t 
     }
 }
 
+// ------------------------------------- bf16 logits, wide tiles (N_r >= 192)
+// Work-group tile: 64 tokens x 256 experts, so the token rows are read once
+// per 256 experts (the 64 x 64 kernel above reads them once per 64).  Tiles of
+// 64-deep k travel memory -> LDS by direct DMA (no staging registers) in a ring
+// of 3 stages, 2 k-tiles ahead; LDS rows of 64 bf16 hold their 16-byte chunks
+// XOR-swizzled (swz).  Wave w owns experts 64 w .. 64 w + 63 of the tile for
+// all 64 tokens: 2 x 2 tiles of the 32x32x16 bf16 matrix-core instruction with
+// the expert fragment as the first operand, so lane l accumulates token l % 32
+// and, in register 4 q + c, expert 8 q + 4 (l / 32) + c of each 32 x 32 tile.
+// The fp32 chunk sums (one 64-deep k-tile: ROUTER_CHUNK products) are added
+// into fp64 after every k-tile, in k order, as the 64 x 64 kernel does, so the
+// same error bound holds.  The kernel serves token counts whose wide tiles
+// fill the chip by themselves (no split-K), and it also writes each token's
+// squared norm (work-groups of the first expert block, from the token tiles in
+// LDS) and the router rows' norms (work-group (b, y) takes expert rows
+// y * 256 + 4 b + w, y * 256 + 4 (b + gridDim.x) + w, ... from memory).
+#define RW_BM 64
+#define RW_BN 256
+#define RW_MIN_EXPERTS 192  // the wide tiles serve layers with at least this many routed experts
+#define RW_MIN_TILES 256    // ... and token counts with at least this many wide tiles
+
+template <int S>
+__device__ __forceinline__ uint16_t *rw_stage_a();
+template <int S>
+__device__ __forceinline__ uint16_t *rw_stage_b();
+__shared__ __attribute__((aligned(16))) uint16_t rw_A0[RW_BM * RT_BK];
+__shared__ __attribute__((aligned(16))) uint16_t rw_A1[RW_BM * RT_BK];
+__shared__ __attribute__((aligned(16))) uint16_t rw_A2[RW_BM * RT_BK];
+__shared__ __attribute__((aligned(16))) uint16_t rw_B0[RW_BN * RT_BK];
+__shared__ __attribute__((aligned(16))) uint16_t rw_B1[RW_BN * RT_BK];
+__shared__ __attribute__((aligned(16))) uint16_t rw_B2[RW_BN * RT_BK];
+template <> __device__ __forceinline__ uint16_t *rw_stage_a<0>() { return rw_A0; }
+template <> __device__ __forceinline__ uint16_t *rw_stage_a<1>() { return rw_A1; }
+template <> __device__ __forceinline__ uint16_t *rw_stage_a<2>() { return rw_A2; }
+template <> __device__ __forceinline__ uint16_t *rw_stage_b<0>() { return rw_B0; }
+template <> __device__ __forceinline__ uint16_t *rw_stage_b<1>() { return rw_B1; }
+template <> __device__ __forceinline__ uint16_t *rw_stage_b<2>() { return rw_B2; }
+
+struct RwArgs {
+  const uint16_t *u, *w;
+  const float *bias;
+  int64_t T;
+  int E, d;
+  double *logits;    // [T, E]
+  double *unorm2;    // [T] squared token norms
+  double *wnorm;     // [E] router row norms
+};
+
+// DMA of k-tile kt into stage S: lane l of wave w fills, for group q, LDS row
+// 32 q + 8 w + l / 8 (A: q < 2, B: q < 8) with global chunk (l % 8) ^ swz(row)
+// of that row.  The rows were clamped into the matrix when the offsets were
+// made (rows past T or E are loaded, never stored).
+template <int S>
+__device__ __forceinline__ void rw_issue(const __amdgpu_buffer_rsrc_t &ra, const __amdgpu_buffer_rsrc_t &rb,
+                                         const uint32_t (&aoff)[2], const uint32_t (&boff)[8], int kt) {
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ko = kt * RT_BK * 2;
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(rw_stage_a<S>() + (32 * q + 8 * wv) * RT_BK), 16,
+                                             (int)aoff[q], ko, 0, 0);
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(rw_stage_b<S>() + (32 * q + 8 * wv) * RT_BK), 16,
+                                             (int)boff[q], ko, 0, 0);
+}
+
+// element offset of 16-byte chunk c of row r in a stage
+__device__ __forceinline__ int rw_off(int r, int c) { return r * RT_BK + ((c ^ swz(r)) << 3); }
+
+// One k-tile from stage S: 4 steps of 16, each 2 expert fragments x 2 token
+// fragments; with NORM, this wave also adds its 16 tokens' squares (lane l:
+// token 16 w + l / 4, elements 16 (l % 4) .. + 15) to nrm.
+template <int S, bool NORM>
+__device__ __forceinline__ void rw_compute(f32x16_t (&acc)[2][2], double &nrm) {
+  const uint16_t *As = rw_stage_a<S>();
+  const uint16_t *Bs = rw_stage_b<S>();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int ch = st * 2 + (lane >> 5);
+    bf16x8_t a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a[i] = as_bf16x8(*(const uint4 *)&As[rw_off(32 * i + (lane & 31), ch)]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[j] = as_bf16x8(*(const uint4 *)&Bs[rw_off(64 * wv + 32 * j + (lane & 31), ch)]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+  }
+  if (NORM) {
+    const int r = 16 * wv + (lane >> 2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 v = *(const uint4 *)&As[rw_off(r, 2 * (lane & 3) + h)];
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double lo = (double)__uint_as_float(w4[q] << 16), hi = (double)__uint_as_float(w4[q] & 0xffff0000u);
+        nrm = fma(lo, lo, nrm);
+        nrm = fma(hi, hi, nrm);
+      }
+    }
+  }
+}
+
+// fp32 chunk sums into the fp64 totals (in k order); the chunk accumulators restart
+__device__ __forceinline__ void rw_flush(f32x16_t (&acc)[2][2], double (&acc64)[2][2][16]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc64[i][j][r] += (double)acc[i][j][r];
+      acc[i][j] = f32x16_t{};
+    }
+}
+
+// k-tile j from stage S = j % 3: wait until k-tile j has landed
+// (the 10 DMA instructions of k-tile j + 1 may still be in flight) and every
+// wave is past its reads of k-tile j - 1, refill that stage with k-tile j + 2,
+// then the MFMAs and the flush.  Every trip issues its DMA, the last two
+// re-loading the final k-tile into stages nothing reads again: with
+// no DMA left out on any path, the compiler's per-stage tracking of pending
+// LDS writes stays exact and it inserts no waits of its own before the
+// fragment reads.
+template <int S, bool NORM>
+__device__ __forceinline__ void rw_iter(const __amdgpu_buffer_rsrc_t &ra, const __amdgpu_buffer_rsrc_t &rb,
+                                        const uint32_t (&aoff)[2], const uint32_t (&boff)[8], int j, int n,
+                                        f32x16_t (&acc)[2][2], double (&acc64)[2][2][16], double &nrm) {
+  publish<10>();
+  rw_issue<(S + 2) % 3>(ra, rb, aoff, boff, min(j + 2, n - 1));
+  rw_compute<S, NORM>(acc, nrm);
+  rw_flush(acc, acc64);
+}
+
+template <bool NORM>
+__device__ __forceinline__ void rw_loop(const __amdgpu_buffer_rsrc_t &ra, const __amdgpu_buffer_rsrc_t &rb,
+                                        const uint32_t (&aoff)[2], const uint32_t (&boff)[8], int n,
+                                        double (&acc64)[2][2][16], double &nrm) {
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+  rw_issue<0>(ra, rb, aoff, boff, 0);
+  rw_issue<1>(ra, rb, aoff, boff, min(1, n - 1));
+  int j = 0;
+  for (; j + 3 <= n; j += 3) {
+    rw_iter<0, NORM>(ra, rb, aoff, boff, j, n, acc, acc64, nrm);
+    rw_iter<1, NORM>(ra, rb, aoff, boff, j + 1, n, acc, acc64, nrm);
+    rw_iter<2, NORM>(ra, rb, aoff, boff, j + 2, n, acc, acc64, nrm);
+  }
+  if (j < n) rw_iter<0, NORM>(ra, rb, aoff, boff, j, n, acc, acc64, nrm);
+  if (j + 1 < n) rw_iter<1, NORM>(ra, rb, aoff, boff, j + 1, n, acc, acc64, nrm);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the re-loads land before the work-group ends
+}
+
+__global__ __launch_bounds__(256, 1) void router_logits_wide_kernel(RwArgs a) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * RW_BM;
+  const int e0 = blockIdx.y * RW_BN;
+  const int n = a.d / RT_BK;
+  // buffer resources over the tile's 64 token rows and 256 router rows, so
+  // that the 32-bit offsets never exceed them (rows clamped into the matrix)
+  const int64_t tr = min((int64_t)RW_BM, a.T - t0);
+  const int er = min(RW_BN, a.E - e0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.u + t0 * a.d, (uint64_t)tr * a.d * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.w + (int64_t)e0 * a.d, (uint64_t)er * a.d * 2);
+  uint32_t aoff[2], boff[8];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 32 * q + 8 * wv + (lane >> 3);
+    aoff[q] = (uint32_t)(min((int64_t)row, tr - 1) * a.d * 2 + (((lane & 7) ^ swz(row)) << 4));
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = 32 * q + 8 * wv + (lane >> 3);
+    boff[q] = (uint32_t)((int64_t)min(row, er - 1) * a.d * 2 + (((lane & 7) ^ swz(row)) << 4));
+  }
+  double acc64[2][2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc64[i][j][r] = 0.0;
+  double nrm = 0.0;
+  const bool norms = blockIdx.y == 0;
+  if (norms) rw_loop<true>(ra, rb, aoff, boff, n, acc64, nrm);
+  else rw_loop<false>(ra, rb, aoff, boff, n, acc64, nrm);
+
+  // logits (bias added): lane l, tile (i, j), registers 4 q .. 4 q + 3: token
+  // 32 i + l % 32, experts e .. e + 3 with e = 64 w + 32 j + 8 q + 4 (l / 32)
+  // of the tile, 32 contiguous bytes of the token's row
+  const bool vec = (a.E & 1) == 0;  // rows of even length keep e (a multiple of 4) 16-byte aligned
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t t = t0 + 32 * i + (lane & 31);
+    if (t >= a.T) continue;
+    double *row = a.logits + t * a.E;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = e0 + 64 * wv + 32 * j + 8 * q + 4 * (lane >> 5);
+        double v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          v[c] = acc64[i][j][4 * q + c] + ((a.bias && e + c < a.E) ? (double)a.bias[e + c] : 0.0);
+        if (vec && e + 3 < a.E) {
+          *(double2 *)(row + e) = make_double2(v[0], v[1]);
+          *(double2 *)(row + e + 2) = make_double2(v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (e + c < a.E) row[e + c] = v[c];
+        }
+      }
+  }
+  if (norms) {
+    nrm += __shfl_xor(nrm, 1, 64);
+    nrm += __shfl_xor(nrm, 2, 64);
+    const int64_t t = t0 + 16 * wv + (lane >> 2);
+    if ((lane & 3) == 0 && t < a.T) a.unorm2[t] = nrm;
+  }
+  // router row norms: rows e0 + 4 b + w, e0 + 4 (b + gridDim.x) + w, ... of
+  // this expert block, one wave each
+  for (int e = e0 + (int)blockIdx.x * 4 + wv; e < e0 + er; e += (int)gridDim.x * 4) {
+    double s2 = 0.0;
+    const uint16_t *p = a.w + (int64_t)e * a.d;
+    for (int i = lane * 8; i < a.d; i += 512) {
+      const uint4 v = *(const uint4 *)(p + i);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double lo = (double)__uint_as_float(w4[q] << 16), hi = (double)__uint_as_float(w4[q] & 0xffff0000u);
+        s2 += lo * lo + hi * hi;
+      }
+    }
+    s2 = wave_sum_f64(s2);
+    if (lane == 0) a.wnorm[e] = sqrt(s2);
+  }
+}
+
 // logits[t, e] = sum over slices s = 0, 1, ... of part[s][t][e] (in this
 // order) + b_e.
 __global__ __launch_bounds__(256) void router_reduce_kernel(const double *__restrict__ part, int S, int64_t n, int E,
@@ -224,11 +470,19 @@ hipError_t launch_router_logits(const moe_dims &dm, int64_t T, const void *u, co
   double *un2 = (double *)(ws + L.unorm2);
   double *wn = (double *)(ws + L.wnorm);
   if (dm.dtype == MOE_BF16) {
-    row_norm2_kernel<true><<<dim3((unsigned)((T + 3) / 4)), 256, 0, st>>>(u, T, d, un2);
-    row_norm2_kernel<true, true><<<dim3((unsigned)((E + 3) / 4)), 256, 0, st>>>(w_router, E, d, wn);
     const int nk = d / RT_BK;
     const int S = router_splits(dm, T);
     const int kps = (nk + S - 1) / S;
+    const int64_t wide_tiles = ((T + RW_BM - 1) / RW_BM) * ((E + RW_BN - 1) / RW_BN);
+    if (E >= RW_MIN_EXPERTS && wide_tiles >= RW_MIN_TILES) {
+      // wide tiles fill the chip without split-K; the norms come out of the same kernel
+      RwArgs ra{(const uint16_t *)u, (const uint16_t *)w_router, bias, T, E, d, logits, un2, wn};
+      dim3 grid((unsigned)((T + RW_BM - 1) / RW_BM), (unsigned)((E + RW_BN - 1) / RW_BN));
+      router_logits_wide_kernel<<<grid, 256, 0, st>>>(ra);
+      return hipGetLastError();
+    }
+    row_norm2_kernel<true><<<dim3((unsigned)((T + 3) / 4)), 256, 0, st>>>(u, T, d, un2);
+    row_norm2_kernel<true, true><<<dim3((unsigned)((E + 3) / 4)), 256, 0, st>>>(w_router, E, d, wn);
     dim3 grid((unsigned)((T + RT_BM - 1) / RT_BM), (unsigned)((E + RT_BN - 1) / RT_BN), (unsigned)S);
     double *part = S > 1 ? (double *)(ws + L.logit_part) : logits;
     router_logits_bf16_kernel<<<grid, 256, 0, st>>>((const uint16_t *)u, (const uint16_t *)w_router, bias, T, E, d,

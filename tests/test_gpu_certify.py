@@ -32,12 +32,12 @@ def _bf16(x: np.ndarray) -> np.ndarray:
     return torch.from_numpy(x).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
 
 
-def _level1_bound(u_row: np.ndarray, c: np.ndarray, logit: np.ndarray, d: int) -> np.ndarray:
+def _level1_bound(u_row: np.ndarray, cnorm: np.ndarray, logit: np.ndarray, d: int) -> np.ndarray:
     """First-level bound of each expert's logit for one token, as the router
     states it: (64 * 2^-22 + (d / 64 + 2) * 2^-52) * ||u|| ||c_e|| (1 + 2^-30)
-    + 2^-50 |L| + d * 2^-120."""
+    + 2^-50 |L| + d * 2^-120, with cnorm[e] = ||c_e||."""
     c1 = 64 * 2.0 ** -22 + (d / 64 + 2) * 2.0 ** -52
-    return (c1 * np.linalg.norm(u_row) * np.linalg.norm(c, axis=1) * (1 + 2.0 ** -30)
+    return (c1 * np.linalg.norm(u_row) * cnorm * (1 + 2.0 ** -30)
             + 2.0 ** -50 * np.abs(logit) + d * 2.0 ** -120)
 
 
@@ -66,13 +66,14 @@ def _cancelling_inputs(E: int, k: int, d: int, per_ratio: int, ties: int, seed: 
         c[:, lo:lo + 32] = y
         c[:, lo + 32:lo + 64] = -y
     c[np.arange(E), d - ncar + np.arange(E)] = 1.0   # expert e's exact logit is u[t, d - ncar + e]
+    cnorm = np.linalg.norm(c, axis=1)
 
     for t, ratio in enumerate(ratios):
         order = rng.permutation(E)      # order[r] is the expert meant for rank r
         v = np.zeros(E)
         for it in range(8):             # the carriers enter ||u||: iterate to the fixed point
             u[t, d - ncar:d - ncar + E] = v
-            B = _level1_bound(u[t], c, v, d)
+            B = _level1_bound(u[t], cnorm, v, d)
             bm = B.max()
             # ranks above k: 3 bounds apart; below k + 1: 8 bounds down (all equal);
             # the carriers stay small against the cancelling part's norm
@@ -90,17 +91,19 @@ def _cancelling_inputs(E: int, k: int, d: int, per_ratio: int, ties: int, seed: 
 
 
 @pytest.mark.parametrize("E,k,d,per_ratio,ties", [
-    (8, 2, 512, 40, 8),       # few tokens: the router's split-K path
-    (256, 8, 1024, 1400, 100),  # 4300 tokens x 256 experts: one reduction slice
-], ids=["E8k2_splitk", "E256k8"])
+    (8, 2, 512, 40, 8),          # few tokens: the router's split-K path
+    (256, 8, 1024, 1400, 100),   # 4300 tokens x 256 experts: 64 x 64 tiles, one reduction slice
+    (256, 8, 1024, 5400, 200),   # 16400 tokens: the wide tiles (64 tokens x 256 experts) and their fused norms
+], ids=["E8k2_splitk", "E256k8", "E256k8_wide"])
 def test_certification_under_cancellation(lib, E, k, d, per_ratio, ties):
     u, c, exact, ratios = _cancelling_inputs(E, k, d, per_ratio, ties, seed=11)
     T = u.shape[0]
+    cnorm = np.linalg.norm(c, axis=1)
     # the placed gaps, measured against the bound of the exact logits
     srt = -np.sort(-exact, axis=1)
     gap = srt[:, k - 1] - srt[:, k]
     for t in range(T):
-        B = _level1_bound(u[t], c, exact[t], d)
+        B = _level1_bound(u[t], cnorm, exact[t], d)
         top = np.argsort(-exact[t], kind="stable")
         got = gap[t] / (B[top[k - 1]] + B[top[k]])
         assert abs(got - ratios[t]) <= 0.01 * max(ratios[t], 1.0), (t, got, ratios[t])

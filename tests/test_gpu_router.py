@@ -1,0 +1,51 @@
+"""GPU parity of the router's wide tiles (64 tokens x 256 experts per work-group).
+
+The bf16 router takes these tiles when they alone give at least 256
+work-groups, with at least 192 routed experts.  The cases below sit just past
+that threshold with ragged token counts, expert counts that leave the last
+expert tile partly empty or span two tiles, an odd expert count (scalar logit
+stores), and depths of 1, 2, 3 and 5 k-tiles of 64 (every path through the
+3-stage ring).  Routing is compared with the oracle on every token, bit for
+bit, and the kept gates to the usual tolerance.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from fine_grained_routed_amd import MoELayer
+from tests.parity import GATE_TOL, gpu_inputs, log, oracle_args
+
+pytestmark = pytest.mark.gpu
+
+# name, T, d, E, k, bias
+CASES = [
+    ("E200_d256", 16384 + 29, 256, 200, 6, "zipf1.2"),
+    ("E300_d192", 8192 + 7, 192, 300, 4, None),
+    ("E255_d128", 16384 + 1, 128, 255, 8, "zipf1.2"),
+    ("E256_d64", 16384 + 63, 64, 256, 8, None),
+    ("E512_d320", 8192 + 33, 320, 512, 10, "zipf1.2"),
+]
+
+
+def _wide_tiles(T: int, E: int) -> int:
+    return -(-T // 64) * -(-E // 256)
+
+
+@pytest.mark.parametrize("name,T,d,E,k,bias", CASES, ids=[c[0] for c in CASES])
+def test_wide_router_tiles_match_the_oracle(lib, name, T, d, E, k, bias):
+    assert E >= 192 and _wide_tiles(T, E) >= 256  # the case takes the wide tiles
+    wl = workloads.Workload(name, T, d, E, 64, 1, k, "bf16", bias, f"router_{name}", "router wide tiles")
+    inp = gpu_inputs(wl, seed=5)
+    layer = MoELayer({kk: vv for kk, vv in inp.items() if kk != "u"}, k)
+    idx, gw = layer.router_topk(inp["u"])
+    diag = layer.diagnostics()
+    a = oracle_args(inp)
+    idx_o, gw_o, _, n_exact = oracle.route(workloads.to_f64(inp["u"]), a["w_router"], k, a["bias"])
+    idx_g = idx.cpu().numpy()
+    bad = np.nonzero((idx_g != idx_o).any(axis=1))[0]
+    log(f"[router] {name} T={T}: {bad.size} tokens differ; diagnostics {diag}, oracle exact {n_exact}")
+    assert bad.size == 0, (bad[:5], idx_g[bad[:3]], idx_o[bad[:3]])
+    gerr = float(np.max(np.abs(gw.cpu().numpy().astype(np.float64) - gw_o)))
+    assert gerr <= GATE_TOL, gerr
+    assert diag["flags"] == 0, diag
