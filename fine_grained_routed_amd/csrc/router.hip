@@ -175,19 +175,22 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const uint16_t 
 // per 256 experts (the 64 x 64 kernel above reads them once per 64).  Tiles of
 // 64-deep k travel memory -> LDS by direct DMA (no staging registers) in a ring
 // of 3 stages, 2 k-tiles ahead; LDS rows of 64 bf16 hold their 16-byte chunks
-// XOR-swizzled (swz).  Wave w owns experts 64 w .. 64 w + 63 of the tile for
-// all 64 tokens: 2 x 2 tiles of the 32x32x16 bf16 matrix-core instruction with
-// the expert fragment as the first operand, so lane l accumulates token l % 32
-// and, in register 4 q + c, expert 8 q + 4 (l / 32) + c of each 32 x 32 tile.
-// The fp32 chunk sums (one 64-deep k-tile: ROUTER_CHUNK products) are added
-// into fp64 after every k-tile, in k order, as the 64 x 64 kernel does, so the
-// same error bound holds.  The kernel serves token counts whose wide tiles
-// fill the chip by themselves (no split-K), and it also writes each token's
-// squared norm (work-groups of the first expert block, from the token tiles in
-// LDS) and the router rows' norms (work-group (b, y) takes expert rows
-// y * 256 + 4 b + w, y * 256 + 4 (b + gridDim.x) + w, ... from memory).
+// XOR-swizzled (swz).  Eight waves, two per SIMD, so that one wave's fp64
+// additions overlap the other's matrix-core work: wave w owns experts
+// 32 w .. 32 w + 31 of the tile for all 64 tokens, two tiles of the 32x32x16
+// bf16 matrix-core instruction with the expert fragment as the first operand,
+// so lane l accumulates token l % 32 and, in register 4 q + c, expert
+// 8 q + 4 (l / 32) + c of each 32 x 32 tile.  The fp32 chunk sums (one 64-deep
+// k-tile: ROUTER_CHUNK products) are added into fp64 after every k-tile, in k
+// order, as the 64 x 64 kernel does, so the same error bound holds.  The
+// kernel serves token counts whose wide tiles fill the chip by themselves (no
+// split-K), and it also writes each token's squared norm (work-groups of the
+// first expert block, from the token tiles in LDS) and the router rows' norms
+// (work-group (b, y) takes expert rows y * 256 + 8 b + w,
+// y * 256 + 8 (b + gridDim.x) + w, ... from memory).
 #define RW_BM 64
 #define RW_BN 256
+#define RW_WAVES 8
 #define RW_MIN_EXPERTS 192  // the wide tiles serve layers with at least this many routed experts
 #define RW_MIN_TILES 256    // ... and token counts with at least this many wide tiles
 
@@ -218,90 +221,79 @@ struct RwArgs {
   double *wnorm;     // [E] router row norms
 };
 
-// DMA of k-tile kt into stage S: lane l of wave w fills, for group q, LDS row
-// 32 q + 8 w + l / 8 (A: q < 2, B: q < 8) with global chunk (l % 8) ^ swz(row)
-// of that row.  The rows were clamped into the matrix when the offsets were
-// made (rows past T or E are loaded, never stored).
+// DMA of k-tile kt into stage S: lane l of wave w fills LDS row 8 w + l / 8 of
+// the A stage and rows 64 q + 8 w + l / 8 (q < 4) of the B stage, each with
+// global chunk (l % 8) ^ swz(row) of that row: five instructions per wave.
+// The rows were clamped into the matrix when the offsets were made (rows past
+// T or E are loaded, never stored).
 template <int S>
 __device__ __forceinline__ void rw_issue(const __amdgpu_buffer_rsrc_t &ra, const __amdgpu_buffer_rsrc_t &rb,
-                                         const uint32_t (&aoff)[2], const uint32_t (&boff)[8], int kt) {
+                                         uint32_t aoff, const uint32_t (&boff)[4], int kt) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ko = kt * RT_BK * 2;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(rw_stage_a<S>() + 8 * wv * RT_BK), 16, (int)aoff, ko,
+                                           0, 0);
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(rw_stage_a<S>() + (32 * q + 8 * wv) * RT_BK), 16,
-                                             (int)aoff[q], ko, 0, 0);
-#pragma unroll
-  for (int q = 0; q < 8; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(rw_stage_b<S>() + (32 * q + 8 * wv) * RT_BK), 16,
+  for (int q = 0; q < 4; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(rw_stage_b<S>() + (64 * q + 8 * wv) * RT_BK), 16,
                                              (int)boff[q], ko, 0, 0);
 }
 
 // element offset of 16-byte chunk c of row r in a stage
 __device__ __forceinline__ int rw_off(int r, int c) { return r * RT_BK + ((c ^ swz(r)) << 3); }
 
-// One k-tile from stage S: 4 steps of 16, each 2 expert fragments x 2 token
-// fragments; with NORM, this wave also adds its 16 tokens' squares (lane l:
-// token 16 w + l / 4, elements 16 (l % 4) .. + 15) to nrm.
+// One k-tile from stage S: 4 steps of 16, each one expert fragment x 2 token
+// fragments; with NORM, this wave also adds the squares of its chunk (lane l:
+// token 8 w + l / 8, elements 8 (l % 8) .. + 7) to nrm.
 template <int S, bool NORM>
-__device__ __forceinline__ void rw_compute(f32x16_t (&acc)[2][2], double &nrm) {
+__device__ __forceinline__ void rw_compute(f32x16_t (&acc)[2], double &nrm) {
   const uint16_t *As = rw_stage_a<S>();
   const uint16_t *Bs = rw_stage_b<S>();
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     const int ch = st * 2 + (lane >> 5);
-    bf16x8_t a[2], b[2];
+    bf16x8_t a[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) a[i] = as_bf16x8(*(const uint4 *)&As[rw_off(32 * i + (lane & 31), ch)]);
+    const bf16x8_t b = as_bf16x8(*(const uint4 *)&Bs[rw_off(32 * wv + (lane & 31), ch)]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b[j] = as_bf16x8(*(const uint4 *)&Bs[rw_off(64 * wv + 32 * j + (lane & 31), ch)]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a[i], acc[i], 0, 0, 0);
   }
   if (NORM) {
-    const int r = 16 * wv + (lane >> 2);
+    const uint4 v = *(const uint4 *)&As[rw_off(8 * wv + (lane >> 3), lane & 7)];
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint4 v = *(const uint4 *)&As[rw_off(r, 2 * (lane & 3) + h)];
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const double lo = (double)__uint_as_float(w4[q] << 16), hi = (double)__uint_as_float(w4[q] & 0xffff0000u);
-        nrm = fma(lo, lo, nrm);
-        nrm = fma(hi, hi, nrm);
-      }
+    for (int q = 0; q < 4; ++q) {
+      const double lo = (double)__uint_as_float(w4[q] << 16), hi = (double)__uint_as_float(w4[q] & 0xffff0000u);
+      nrm = fma(lo, lo, nrm);
+      nrm = fma(hi, hi, nrm);
     }
   }
 }
 
 // fp32 chunk sums into the fp64 totals (in k order); the chunk accumulators restart
-__device__ __forceinline__ void rw_flush(f32x16_t (&acc)[2][2], double (&acc64)[2][2][16]) {
+__device__ __forceinline__ void rw_flush(f32x16_t (&acc)[2], double (&acc64)[2][16]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc64[i][j][r] += (double)acc[i][j][r];
-      acc[i][j] = f32x16_t{};
-    }
+    for (int r = 0; r < 16; ++r) acc64[i][r] += (double)acc[i][r];
+    acc[i] = f32x16_t{};
+  }
 }
 
-// k-tile j from stage S = j % 3: wait until k-tile j has landed
-// (the 10 DMA instructions of k-tile j + 1 may still be in flight) and every
-// wave is past its reads of k-tile j - 1, refill that stage with k-tile j + 2,
-// then the MFMAs and the flush.  Every trip issues its DMA, the last two
-// re-loading the final k-tile into stages nothing reads again: with
-// no DMA left out on any path, the compiler's per-stage tracking of pending
-// LDS writes stays exact and it inserts no waits of its own before the
-// fragment reads.
+// k-tile j from stage S = j % 3: wait until it has landed (the 5 DMA
+// instructions of k-tile j + 1 may still be in flight) and every wave is past
+// its reads of k-tile j - 1, refill that stage with k-tile j + 2, then the
+// MFMAs and the flush.  Every trip issues its DMA, the last two re-loading the
+// final k-tile into stages nothing reads again: with no DMA left out on any
+// path, the compiler's per-stage tracking of pending LDS writes stays exact
+// and it inserts no waits of its own before the fragment reads.
 template <int S, bool NORM>
 __device__ __forceinline__ void rw_iter(const __amdgpu_buffer_rsrc_t &ra, const __amdgpu_buffer_rsrc_t &rb,
-                                        const uint32_t (&aoff)[2], const uint32_t (&boff)[8], int j, int n,
-                                        f32x16_t (&acc)[2][2], double (&acc64)[2][2][16], double &nrm) {
-  publish<10>();
+                                        uint32_t aoff, const uint32_t (&boff)[4], int j, int n,
+                                        f32x16_t (&acc)[2], double (&acc64)[2][16], double &nrm) {
+  publish<5>();
   rw_issue<(S + 2) % 3>(ra, rb, aoff, boff, min(j + 2, n - 1));
   rw_compute<S, NORM>(acc, nrm);
   rw_flush(acc, acc64);
@@ -309,13 +301,9 @@ __device__ __forceinline__ void rw_iter(const __amdgpu_buffer_rsrc_t &ra, const 
 
 template <bool NORM>
 __device__ __forceinline__ void rw_loop(const __amdgpu_buffer_rsrc_t &ra, const __amdgpu_buffer_rsrc_t &rb,
-                                        const uint32_t (&aoff)[2], const uint32_t (&boff)[8], int n,
-                                        double (&acc64)[2][2][16], double &nrm) {
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+                                        uint32_t aoff, const uint32_t (&boff)[4], int n, double (&acc64)[2][16],
+                                        double &nrm) {
+  f32x16_t acc[2] = {f32x16_t{}, f32x16_t{}};
   rw_issue<0>(ra, rb, aoff, boff, 0);
   rw_issue<1>(ra, rb, aoff, boff, min(1, n - 1));
   int j = 0;
@@ -324,12 +312,16 @@ __device__ __forceinline__ void rw_loop(const __amdgpu_buffer_rsrc_t &ra, const 
     rw_iter<1, NORM>(ra, rb, aoff, boff, j + 1, n, acc, acc64, nrm);
     rw_iter<2, NORM>(ra, rb, aoff, boff, j + 2, n, acc, acc64, nrm);
   }
-  if (j < n) rw_iter<0, NORM>(ra, rb, aoff, boff, j, n, acc, acc64, nrm);
-  if (j + 1 < n) rw_iter<1, NORM>(ra, rb, aoff, boff, j + 1, n, acc, acc64, nrm);
+  // each remaining trip is reached only through the one before it, so every
+  // path into a trip carries the same DMA history
+  if (j < n) {
+    rw_iter<0, NORM>(ra, rb, aoff, boff, j, n, acc, acc64, nrm);
+    if (j + 1 < n) rw_iter<1, NORM>(ra, rb, aoff, boff, j + 1, n, acc, acc64, nrm);
+  }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the re-loads land before the work-group ends
 }
 
-__global__ __launch_bounds__(256, 1) void router_logits_wide_kernel(RwArgs a) {
+__global__ __launch_bounds__(64 * RW_WAVES, 1) void router_logits_wide_kernel(RwArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t t0 = (int64_t)blockIdx.x * RW_BM;
   const int e0 = blockIdx.y * RW_BN;
@@ -340,32 +332,27 @@ __global__ __launch_bounds__(256, 1) void router_logits_wide_kernel(RwArgs a) {
   const int er = min(RW_BN, a.E - e0);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.u + t0 * a.d, (uint64_t)tr * a.d * 2);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.w + (int64_t)e0 * a.d, (uint64_t)er * a.d * 2);
-  uint32_t aoff[2], boff[8];
+  const int arow = 8 * wv + (lane >> 3);
+  const uint32_t aoff = (uint32_t)(min((int64_t)arow, tr - 1) * a.d * 2 + (((lane & 7) ^ swz(arow)) << 4));
+  uint32_t boff[4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row = 32 * q + 8 * wv + (lane >> 3);
-    aoff[q] = (uint32_t)(min((int64_t)row, tr - 1) * a.d * 2 + (((lane & 7) ^ swz(row)) << 4));
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int row = 32 * q + 8 * wv + (lane >> 3);
+  for (int q = 0; q < 4; ++q) {
+    const int row = 64 * q + 8 * wv + (lane >> 3);
     boff[q] = (uint32_t)((int64_t)min(row, er - 1) * a.d * 2 + (((lane & 7) ^ swz(row)) << 4));
   }
-  double acc64[2][2][16];
+  double acc64[2][16];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc64[i][j][r] = 0.0;
+    for (int r = 0; r < 16; ++r) acc64[i][r] = 0.0;
   double nrm = 0.0;
   const bool norms = blockIdx.y == 0;
   if (norms) rw_loop<true>(ra, rb, aoff, boff, n, acc64, nrm);
   else rw_loop<false>(ra, rb, aoff, boff, n, acc64, nrm);
 
-  // logits (bias added): lane l, tile (i, j), registers 4 q .. 4 q + 3: token
-  // 32 i + l % 32, experts e .. e + 3 with e = 64 w + 32 j + 8 q + 4 (l / 32)
-  // of the tile, 32 contiguous bytes of the token's row
+  // logits (bias added): lane l, tile i, registers 4 q .. 4 q + 3: token
+  // 32 i + l % 32, experts e .. e + 3 with e = 32 w + 8 q + 4 (l / 32) of the
+  // tile, 32 contiguous bytes of the token's row
   const bool vec = (a.E & 1) == 0;  // rows of even length keep e (a multiple of 4) 16-byte aligned
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -373,33 +360,32 @@ __global__ __launch_bounds__(256, 1) void router_logits_wide_kernel(RwArgs a) {
     if (t >= a.T) continue;
     double *row = a.logits + t * a.E;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int q = 0; q < 4; ++q) {
+      const int e = e0 + 32 * wv + 8 * q + 4 * (lane >> 5);
+      double v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = e0 + 64 * wv + 32 * j + 8 * q + 4 * (lane >> 5);
-        double v[4];
+      for (int c = 0; c < 4; ++c)
+        v[c] = acc64[i][4 * q + c] + ((a.bias && e + c < a.E) ? (double)a.bias[e + c] : 0.0);
+      if (vec && e + 3 < a.E) {
+        *(double2 *)(row + e) = make_double2(v[0], v[1]);
+        *(double2 *)(row + e + 2) = make_double2(v[2], v[3]);
+      } else {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          v[c] = acc64[i][j][4 * q + c] + ((a.bias && e + c < a.E) ? (double)a.bias[e + c] : 0.0);
-        if (vec && e + 3 < a.E) {
-          *(double2 *)(row + e) = make_double2(v[0], v[1]);
-          *(double2 *)(row + e + 2) = make_double2(v[2], v[3]);
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (e + c < a.E) row[e + c] = v[c];
-        }
+          if (e + c < a.E) row[e + c] = v[c];
       }
+    }
   }
   if (norms) {
     nrm += __shfl_xor(nrm, 1, 64);
     nrm += __shfl_xor(nrm, 2, 64);
-    const int64_t t = t0 + 16 * wv + (lane >> 2);
-    if ((lane & 3) == 0 && t < a.T) a.unorm2[t] = nrm;
+    nrm += __shfl_xor(nrm, 4, 64);
+    const int64_t t = t0 + 8 * wv + (lane >> 3);
+    if ((lane & 7) == 0 && t < a.T) a.unorm2[t] = nrm;
   }
-  // router row norms: rows e0 + 4 b + w, e0 + 4 (b + gridDim.x) + w, ... of
+  // router row norms: rows e0 + 8 b + w, e0 + 8 (b + gridDim.x) + w, ... of
   // this expert block, one wave each
-  for (int e = e0 + (int)blockIdx.x * 4 + wv; e < e0 + er; e += (int)gridDim.x * 4) {
+  for (int e = e0 + (int)blockIdx.x * RW_WAVES + wv; e < e0 + er; e += (int)gridDim.x * RW_WAVES) {
     double s2 = 0.0;
     const uint16_t *p = a.w + (int64_t)e * a.d;
     for (int i = lane * 8; i < a.d; i += 512) {
@@ -478,7 +464,7 @@ hipError_t launch_router_logits(const moe_dims &dm, int64_t T, const void *u, co
       // wide tiles fill the chip without split-K; the norms come out of the same kernel
       RwArgs ra{(const uint16_t *)u, (const uint16_t *)w_router, bias, T, E, d, logits, un2, wn};
       dim3 grid((unsigned)((T + RW_BM - 1) / RW_BM), (unsigned)((E + RW_BN - 1) / RW_BN));
-      router_logits_wide_kernel<<<grid, 256, 0, st>>>(ra);
+      router_logits_wide_kernel<<<grid, 64 * RW_WAVES, 0, st>>>(ra);
       return hipGetLastError();
     }
     row_norm2_kernel<true><<<dim3((unsigned)((T + 3) / 4)), 256, 0, st>>>(u, T, d, un2);
