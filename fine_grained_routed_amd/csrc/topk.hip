@@ -116,45 +116,93 @@ __device__ void exact_key(const void *urow, const void *w, const float *bias, in
 
 // Wave-cooperative fp64 logit of expert e (uniform result): exact products,
 // fp64 sums.  16-byte loads: lane l takes the 8 (bf16) or 4 (fp32) elements
-// of chunk l, l + 64, ... (d is a multiple of 64).
+// of chunk l, l + 64, ... (d is a multiple of 64), DOT_BATCH chunks of each
+// row in flight at once, into two accumulators (each lane's chain of
+// additions only gets shorter than the d / 64 the fp64 bound allows for).
+#define DOT_BATCH 4
 template <bool BF16>
 __device__ double dot_f64(const void *urow, const void *w, const float *bias, int e, int d) {
   const int lane = threadIdx.x & 63;
-  double acc = 0.0;
-  if (BF16) {
-    const uint4 *up = (const uint4 *)urow;
-    const uint4 *wp = (const uint4 *)((const uint16_t *)w + (int64_t)e * d);
-    for (int c = lane; c < d / 8; c += 64) {
-      const uint4 a = up[c], b = wp[c];
-      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+  double acc[2] = {0.0, 0.0};
+  const int nc = BF16 ? d / 8 : d / 4;  // 16-byte chunks per row
+  const uint4 *up = (const uint4 *)urow;
+  const uint4 *wp = BF16 ? (const uint4 *)((const uint16_t *)w + (int64_t)e * d)
+                         : (const uint4 *)((const float *)w + (int64_t)e * d);
+  for (int c0 = lane; c0 < nc; c0 += 64 * DOT_BATCH) {
+    uint4 a[DOT_BATCH], b[DOT_BATCH];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc = fma((double)__uint_as_float(av[q] << 16), (double)__uint_as_float(bv[q] << 16), acc);
-        acc = fma((double)__uint_as_float(av[q] & 0xffff0000u), (double)__uint_as_float(bv[q] & 0xffff0000u), acc);
+    for (int q = 0; q < DOT_BATCH; ++q) {
+      const int c = c0 + 64 * q;
+      a[q] = c < nc ? up[c] : make_uint4(0, 0, 0, 0);  // zero chunks add exact zeros
+      b[q] = c < nc ? wp[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < DOT_BATCH; ++q) {
+      const uint32_t av[4] = {a[q].x, a[q].y, a[q].z, a[q].w}, bv[4] = {b[q].x, b[q].y, b[q].z, b[q].w};
+      double &r = acc[q & 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (BF16) {
+          r = fma((double)__uint_as_float(av[i] << 16), (double)__uint_as_float(bv[i] << 16), r);
+          r = fma((double)__uint_as_float(av[i] & 0xffff0000u), (double)__uint_as_float(bv[i] & 0xffff0000u), r);
+        } else {
+          r = fma((double)__uint_as_float(av[i]), (double)__uint_as_float(bv[i]), r);
+        }
       }
     }
-  } else {
-    const float4 *up = (const float4 *)urow;
-    const float4 *wp = (const float4 *)((const float *)w + (int64_t)e * d);
-    for (int c = lane; c < d / 4; c += 64) {
-      const float4 a = up[c], b = wp[c];
-      acc = fma((double)a.x, (double)b.x, acc);
-      acc = fma((double)a.y, (double)b.y, acc);
-      acc = fma((double)a.z, (double)b.z, acc);
-      acc = fma((double)a.w, (double)b.w, acc);
-    }
   }
-  acc = wave_sum_f64(acc);
-  if (bias) acc += (double)bias[e];
-  return acc;
+  double v = wave_sum_f64(acc[0] + acc[1]);
+  if (bias) v += (double)bias[e];
+  return v;
 }
 
 // Lowest expert index among the set bits of `bits` (bit s of lane l = expert
-// l + 64 s) over the wave, or a large value when no bit is set.
+// l + 64 s) over the wave, or a large value when no bit is set: one ballot
+// per register slot.
+template <int S>
 __device__ __forceinline__ int lowest_expert(unsigned bits) {
-  const int lane = threadIdx.x & 63;
-  const int my = bits ? lane + 64 * (__ffs(bits) - 1) : 0x7fffffff;
-  return wave_min_i32(my);
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const unsigned long long b = __ballot((bits >> s) & 1u);
+    if (b) return (__ffsll((long long)b) - 1) + 64 * s;
+  }
+  return 0x7fffffff;
+}
+
+// Wave-wide fp64 max and sum with the same value in every lane: four DPP
+// steps (lane i meets lanes i ^ 1, i ^ 2, then its mirror in 8 and in 16)
+// leave every row of 16 lanes holding its row's result, and the four rows
+// are combined from lanes 0, 16, 32, 48.  Each step pairs a lane with a
+// partner that holds the same partial set, so every lane's sums see the same
+// operands (in swapped order) and agree bit for bit.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, l), hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+__device__ __forceinline__ double row_max_f64(double v) {
+  v = fmax(v, dpp_f64<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = fmax(v, dpp_f64<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = fmax(v, dpp_f64<0x141>(v));  // row_half_mirror
+  return fmax(v, dpp_f64<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ double dpp_wave_max_f64(double v) {
+  v = row_max_f64(v);
+  return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+__device__ __forceinline__ double dpp_wave_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x141>(v);
+  v += dpp_f64<0x140>(v);
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 template <int S, bool BF16>
@@ -188,12 +236,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
   double mx = NEG;
 #pragma unroll
   for (int s = 0; s < S; ++s) mx = fmax(mx, L[s]);
-  mx = wave_max_f64(mx);
+  mx = dpp_wave_max_f64(mx);
   double sum = 0.0;
 #pragma unroll
   for (int s = 0; s < S; ++s)
     if (avail & (1u << s)) sum += (double)expf((float)(L[s] - mx));
-  sum = wave_sum_f64(sum);
+  sum = dpp_wave_sum_f64(sum);
 
   const void *urow = BF16 ? (const void *)((const uint16_t *)u + t * d) : (const void *)((const float *)u + t * d);
   bool token_exact = false;
@@ -210,26 +258,25 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
 #pragma unroll
       for (int s = 0; s < S; ++s)
         if (avail & (1u << s)) mlo = fmax(mlo, L[s] - B[s]);
-      mlo = wave_max_f64(mlo);
+      mlo = dpp_wave_max_f64(mlo);
       unsigned member = 0;
 #pragma unroll
       for (int s = 0; s < S; ++s)
         if ((avail & (1u << s)) && L[s] + B[s] >= mlo) member |= 1u << s;
-      const int cnt = wave_sum_i32(__popc(member));
-      if (cnt == 1) {
-        int my = -1;
-#pragma unroll
-        for (int s = 0; s < S; ++s)
-          if (member & (1u << s)) my = lane + 64 * s;
-        win = wave_max_i32(my);
+      const int mine = __popc(member);
+      const unsigned long long holders = __ballot(mine > 0);
+      if (__popcll(holders) == 1 && __ballot(mine > 1) == 0) {
+        // a single member: the one lane holding one, in its lowest set slot
+        const int my = member ? lane + 64 * (__ffs(member) - 1) : 0;
+        win = __builtin_amdgcn_readlane(my, __ffsll((long long)holders) - 1);
         break;
       }
       token_exact = true;
       unsigned need = member & ~refined;
-      if (wave_sum_i32(__popc(need)) > 0) {
+      if (__ballot(need != 0u)) {
         // level 2: fp64 logits of the unrefined members, written back in place
         // (expert e lives in lane e % 64, register slot e / 64)
-        for (int e = lowest_expert(need); e != 0x7fffffff; e = lowest_expert(need)) {
+        for (int e = lowest_expert<S>(need); e != 0x7fffffff; e = lowest_expert<S>(need)) {
           const double l64 = dot_f64<BF16>(urow, w, bias, e, d);
           const double b64 = c64 * su * wn[e] * (1.0 + 0x1p-30) + 0x1p-51 * fabs(l64) + d * 0x1p-120;
 #pragma unroll
@@ -252,7 +299,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
       }
       int ew = -100000, eb = -100000;
       for (unsigned rest = member; ; ) {
-        const int e = lowest_expert(rest);
+        const int e = lowest_expert<S>(rest);
         if (e == 0x7fffffff) break;
         for (int i = lane; i < d; i += 64) ew = max(ew, exponent_of(load_elem<BF16>(w, (int64_t)e * d + i)));
         if (bias) eb = max(eb, exponent_of((double)bias[e]));
@@ -270,7 +317,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
 #pragma unroll
       for (int q = 0; q < EXACT_LIMBS; ++q) best[q] = 0;
       for (unsigned rest = member; ; ) {  // ascending expert order
-        const int e = lowest_expert(rest);
+        const int e = lowest_expert<S>(rest);
         if (e == 0x7fffffff) break;
         if ((e & 63) == lane) rest &= ~(1u << (e >> 6));
         exact_key<BF16>(urow, w, bias, e, d, E0, cur, bad);
@@ -285,6 +332,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
         }
       }
       win = __builtin_amdgcn_readfirstlane(exact_win);
+      const int cnt = wave_sum_i32(mine);
       if (lane == 0) atomicAdd(&diag->exact_keys, (unsigned)cnt);
       break;
     }
@@ -301,25 +349,19 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
         }
       }
     }
-    // take the winner out and emit its slot
-    double lw = NEG;
+    // the winner's lane takes it out and emits its slot
 #pragma unroll
     for (int s = 0; s < S; ++s)
       if (lane + 64 * s == win) {
-        lw = L[s];
         avail &= ~(1u << s);
+        idx_out[t * k + j] = win;
+        w_out[t * k + j] = (float)((double)expf((float)(L[s] - mx)) / sum);
       }
-    lw = wave_max_f64(lw);
-    if (lane == 0) {
-      idx_out[t * k + j] = win;
-      w_out[t * k + j] = (float)((double)expf((float)(lw - mx)) / sum);
-    }
   }
   if (lane == 0) {
     if (token_exact) atomicAdd(&diag->tokens_exact, 1u);
   }
-  bad = (unsigned)wave_max_i32((int)bad);
-  if (lane == 0 && bad) atomicOr(&diag->flags, MOE_DIAG_UNRESOLVED);
+  if (__ballot(bad != 0u) && lane == 0) atomicOr(&diag->flags, MOE_DIAG_UNRESOLVED);
 }
 
 template <int S>
