@@ -129,7 +129,13 @@ struct DiagWords {
   uint32_t tokens_exact;
   uint32_t exact_keys;
   uint32_t refinements;
+  uint32_t deferred;  // tokens the first top-k kernel left to the second (not part of moe_diag)
 };
+
+// Up to this many tokens the cooperative top-k kernel takes every token;
+// above it, the wavefront-per-token kernel first settles the clear ones and
+// lists the rest (int32 [T] in the workspace).
+#define MOE_TOPK_COOP_ALL 1024
 
 // M-tile heights for which the permutation writes per-expert tile prefixes.
 #define MOE_N_BM 5
@@ -168,6 +174,7 @@ struct WsLayout {
   size_t h_sh;        // bf16 or f32 [T, f_s] shared hidden activations
   size_t topk_idx;    // int32 [T, k]  (layer forward only)
   size_t topk_w;      // f32   [T, k]
+  size_t topk_list;   // int32 [T]     tokens left to the cooperative top-k kernel (T > MOE_TOPK_COOP_ALL only)
   size_t counts;      // int32 [N_r]
   size_t offsets;     // int32 [N_r + 1]
   size_t row_token;   // int32 [R]
@@ -247,6 +254,7 @@ static inline WsLayout moe_ws_layout(const moe_dims &dm, int64_t T) {
   L.h_sh = take((size_t)T * fs * hbytes);
   L.topk_idx = take(R * 4);
   L.topk_w = take(R * 4);
+  L.topk_list = take(T > MOE_TOPK_COOP_ALL && E > 0 ? (size_t)T * 4 : 0);
   L.counts = take(E * 4);
   L.offsets = take((E + 1) * 4);
   L.row_token = take(R * 4);

@@ -6,15 +6,15 @@
 // expert index; slot j holds the (j+1)-th largest key.  The kept weights are
 // the full-softmax probabilities (not renormalised over the k kept experts).
 //
-// One wavefront per token.  Each of the k rounds picks the largest remaining
-// key.  With computed logits L_e and bounds B_e (router.hip), let m be the
-// largest lower bound L_e - B_e among the remaining experts; only experts with
-// L_e + B_e >= m can hold the maximum.  When that set has one member it is the
-// winner.  Otherwise its members' logits are recomputed in fp64 (exact
-// products, fp64 sums; bound ~(d/64 + 8) 2^-52 ||u|| ||c||) and written back in
-// place with their tighter bounds, and the round is re-decided.  Members are
-// visited lowest index first by a wave-wide minimum.  Members whose
-// fp64 intervals still overlap are compared exactly: each key becomes a 256-bit
+// Each of the k rounds picks the largest remaining key.  With computed
+// logits L_e and bounds B_e (router.hip), let m be the largest lower bound
+// L_e - B_e among the remaining experts; only experts with L_e + B_e >= m can
+// hold the maximum.  When that set has one member it is the winner.
+// Otherwise its members' logits are recomputed in fp64 (exact products, fp64
+// sums; bound ~(d/64 + 8) 2^-52 ||u|| ||c||) and written back in place with
+// their tighter bounds, and the round is re-decided.  Members are visited
+// lowest index first.  Members whose fp64 intervals still overlap are
+// compared exactly: each key becomes a 256-bit
 // fixed-point sum of its exact products (bf16 x bf16 and fp32 x fp32 products
 // are exact in fp64) and the largest wins, ties to the lower index.  A product
 // that falls below the fixed-point window (a dynamic range above ~2^200 inside
@@ -29,11 +29,27 @@
 // groups that walk meets are exactly the kept groups: from the round that
 // meets the last of them on, every other group's experts leave the candidate
 // set, and every winner is a kept expert.
+//
+// Two kernels.  The first gives each token one wavefront and settles every
+// token whose k rounds all have a single member; a token that needs more is
+// appended to a list and left to the second, which runs the full procedure
+// with one wavefront per listed token.  Batches of up to MOE_TOPK_COOP_ALL
+// tokens skip the first kernel: the second then gives every token a
+// work-group of four wavefronts that all hold the token's logits and take the
+// same decisions, and a refinement splits every member's fp64 dot product
+// over the four, which exchange partial sums through LDS, so that its latency
+// is about a quarter of one wavefront's.  A refinement pass takes up to
+// several members at once, so their loads are in flight together.
 #include "common.h"
 
 double router_bound_coeff(const moe_dims &dm);
 
-#define TOPK_TOKENS_PER_WG 4
+#define TOPK_TOKENS_PER_WG 4   // first kernel: one wavefront per token
+#define TOPK_MEMBERS_1 2       // members per refinement pass, one wavefront per token
+#define TOPK_MEMBERS_4 4       // ... four wavefronts per token
+#define TOPK_DOT_BATCH 4       // 16-byte chunks of a row in flight per lane (second kernel)
+#define TOPK_FAST_BATCH 2      // ... in the first kernel, whose registers set its occupancy
+#define TOPK_LIST_WGS 64       // work-groups of the second kernel over the (usually short) list
 #define EXACT_LIMBS 8  // radix 2^32 digits held in int64 (carry headroom)
 
 template <bool BF16>
@@ -114,46 +130,78 @@ __device__ void exact_key(const void *urow, const void *w, const float *bias, in
   for (int q = 0; q < EXACT_LIMBS; ++q) key[q] = wave_sum_i64(key[q]);
 }
 
-// Wave-cooperative fp64 logit of expert e (uniform result): exact products,
-// fp64 sums.  16-byte loads: lane l takes the 8 (bf16) or 4 (fp32) elements
-// of chunk l, l + 64, ... (d is a multiple of 64), DOT_BATCH chunks of each
-// row in flight at once, into two accumulators (each lane's chain of
-// additions only gets shorter than the d / 64 the fp64 bound allows for).
-#define DOT_BATCH 4
-template <bool BF16>
-__device__ double dot_f64(const void *urow, const void *w, const float *bias, int e, int d) {
-  const int lane = threadIdx.x & 63;
-  double acc[2] = {0.0, 0.0};
+// fp64 logits of up to M experts es[0..m) for the token row urow,
+// by the NW wavefronts (1 or 4) that hold the token (uniform results in every
+// lane of each): exact products, fp64 sums.  16-byte chunk c of a row (8 bf16
+// or 4 fp32 elements) goes to lane c % 64 of wave (c / 64) % NW; a lane adds
+// its chunks in order, the wave sums its lanes and, with four waves, the wave
+// sums are added in wave order through LDS (part), then the bias.  A term
+// passes through at most 8 ceil(d / (512 NW)) + 9 additions, inside the
+// (d / 64 + 8) 2^-52 bound's allowance (which counts 2^-53 per addition
+// twice over) for every d >= 64.
+template <bool BF16, int NW, int M, int DOT_BATCH>
+__device__ void coop_dots(const void *urow, const void *w, const float *bias, const int (&es)[M], int m, int d,
+                          double (*part)[M], double (&out)[M]) {
+  const int lane = threadIdx.x & 63, wv = NW == 1 ? 0 : threadIdx.x >> 6;
   const int nc = BF16 ? d / 8 : d / 4;  // 16-byte chunks per row
   const uint4 *up = (const uint4 *)urow;
-  const uint4 *wp = BF16 ? (const uint4 *)((const uint16_t *)w + (int64_t)e * d)
-                         : (const uint4 *)((const float *)w + (int64_t)e * d);
-  for (int c0 = lane; c0 < nc; c0 += 64 * DOT_BATCH) {
-    uint4 a[DOT_BATCH], b[DOT_BATCH];
+  double acc[M];
 #pragma unroll
-    for (int q = 0; q < DOT_BATCH; ++q) {
-      const int c = c0 + 64 * q;
-      a[q] = c < nc ? up[c] : make_uint4(0, 0, 0, 0);  // zero chunks add exact zeros
-      b[q] = c < nc ? wp[c] : make_uint4(0, 0, 0, 0);
+  for (int q = 0; q < M; ++q) acc[q] = 0.0;
+  for (int c0 = 64 * wv + lane; c0 < nc; c0 += 64 * NW * DOT_BATCH) {
+    uint4 a[DOT_BATCH];
+#pragma unroll
+    for (int i = 0; i < DOT_BATCH; ++i) {
+      const int c = c0 + 64 * NW * i;
+      a[i] = c < nc ? up[c] : make_uint4(0, 0, 0, 0);  // zero chunks add exact zeros
     }
 #pragma unroll
-    for (int q = 0; q < DOT_BATCH; ++q) {
-      const uint32_t av[4] = {a[q].x, a[q].y, a[q].z, a[q].w}, bv[4] = {b[q].x, b[q].y, b[q].z, b[q].w};
-      double &r = acc[q & 1];
+    for (int q = 0; q < M; ++q) {
+      if (q >= m) continue;
+      const uint4 *wp = BF16 ? (const uint4 *)((const uint16_t *)w + (int64_t)es[q] * d)
+                             : (const uint4 *)((const float *)w + (int64_t)es[q] * d);
+      uint4 b[DOT_BATCH];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (BF16) {
-          r = fma((double)__uint_as_float(av[i] << 16), (double)__uint_as_float(bv[i] << 16), r);
-          r = fma((double)__uint_as_float(av[i] & 0xffff0000u), (double)__uint_as_float(bv[i] & 0xffff0000u), r);
-        } else {
-          r = fma((double)__uint_as_float(av[i]), (double)__uint_as_float(bv[i]), r);
+      for (int i = 0; i < DOT_BATCH; ++i) {
+        const int c = c0 + 64 * NW * i;
+        b[i] = c < nc ? wp[c] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < DOT_BATCH; ++i) {
+        const uint32_t av[4] = {a[i].x, a[i].y, a[i].z, a[i].w}, bv[4] = {b[i].x, b[i].y, b[i].z, b[i].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          if (BF16) {
+            acc[q] = fma((double)__uint_as_float(av[h] << 16), (double)__uint_as_float(bv[h] << 16), acc[q]);
+            acc[q] = fma((double)__uint_as_float(av[h] & 0xffff0000u), (double)__uint_as_float(bv[h] & 0xffff0000u),
+                         acc[q]);
+          } else {
+            acc[q] = fma((double)__uint_as_float(av[h]), (double)__uint_as_float(bv[h]), acc[q]);
+          }
         }
       }
     }
   }
-  double v = wave_sum_f64(acc[0] + acc[1]);
-  if (bias) v += (double)bias[e];
-  return v;
+  if (NW == 1) {
+#pragma unroll
+    for (int q = 0; q < M; ++q) {
+      out[q] = wave_sum_f64(acc[q]);
+      if (q < m && bias) out[q] += (double)bias[es[q]];
+    }
+    return;
+  }
+#pragma unroll
+  for (int q = 0; q < M; ++q) {
+    const double v = wave_sum_f64(acc[q]);
+    if (q < m && lane == 0) part[wv][q] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < M; ++q) {
+    out[q] = (part[0][q] + part[1][q]) + (part[2][q] + part[3][q]);
+    if (q < m && bias) out[q] += (double)bias[es[q]];
+  }
+  __syncthreads();  // part is free again
 }
 
 // Lowest expert index among the set bits of `bits` (bit s of lane l = expert
@@ -161,25 +209,25 @@ __device__ double dot_f64(const void *urow, const void *w, const float *bias, in
 // per register slot.
 template <int S>
 __device__ __forceinline__ int lowest_expert(unsigned bits) {
+  int r = 0x7fffffff;
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
+  for (int s = S - 1; s >= 0; --s) {
     const unsigned long long b = __ballot((bits >> s) & 1u);
-    if (b) return (__ffsll((long long)b) - 1) + 64 * s;
+    if (b) r = (__ffsll((long long)b) - 1) + 64 * s;
   }
-  return 0x7fffffff;
+  return r;
 }
 
-// Wave-wide fp64 max and sum with the same value in every lane: four DPP
-// steps (lane i meets lanes i ^ 1, i ^ 2, then its mirror in 8 and in 16)
-// leave every row of 16 lanes holding its row's result, and the four rows
-// are combined from lanes 0, 16, 32, 48.  Each step pairs a lane with a
-// partner that holds the same partial set, so every lane's sums see the same
-// operands (in swapped order) and agree bit for bit.
-template <int CTRL>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xf, 0xf, false);
+// Wave-wide fp64 max and sum, uniform: four DPP steps (lane i meets lanes
+// i ^ 1, i ^ 2, then its mirror in 8 and in 16) leave every row of 16 lanes
+// holding its row's result; two row broadcasts then fold row 0 into row 1,
+// row 2 into row 3 and row 1 into row 3, and lane 63's value is the result.
+// The order of the additions is fixed, so the sum is reproducible.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double old, double v) {
+  const long long o = __double_as_longlong(old), b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp((int)o, (int)b, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(o >> 32), (int)(b >> 32), CTRL, ROWS, 0xf, false);
   return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
 }
 __device__ __forceinline__ double readlane_f64(double v, int l) {
@@ -187,211 +235,377 @@ __device__ __forceinline__ double readlane_f64(double v, int l) {
   const int lo = __builtin_amdgcn_readlane((int)b, l), hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
   return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
 }
-__device__ __forceinline__ double row_max_f64(double v) {
-  v = fmax(v, dpp_f64<0xB1>(v));   // quad_perm [1, 0, 3, 2]
-  v = fmax(v, dpp_f64<0x4E>(v));   // quad_perm [2, 3, 0, 1]
-  v = fmax(v, dpp_f64<0x141>(v));  // row_half_mirror
-  return fmax(v, dpp_f64<0x140>(v));  // row_mirror
-}
+#define DPP_XOR1 0xB1       // quad_perm [1, 0, 3, 2]
+#define DPP_XOR2 0x4E       // quad_perm [2, 3, 0, 1]
+#define DPP_HALF_MIRROR 0x141
+#define DPP_MIRROR 0x140
+#define DPP_BCAST15 0x142   // lane 15 of each row into the next row
+#define DPP_BCAST31 0x143   // lane 31 into rows 2 and 3
 __device__ __forceinline__ double dpp_wave_max_f64(double v) {
-  v = row_max_f64(v);
-  return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+  v = fmax(v, dpp_f64<DPP_XOR1, 0xf>(v, v));
+  v = fmax(v, dpp_f64<DPP_XOR2, 0xf>(v, v));
+  v = fmax(v, dpp_f64<DPP_HALF_MIRROR, 0xf>(v, v));
+  v = fmax(v, dpp_f64<DPP_MIRROR, 0xf>(v, v));
+  v = fmax(v, dpp_f64<DPP_BCAST15, 0xa>(v, v));  // rows outside the mask keep v
+  v = fmax(v, dpp_f64<DPP_BCAST31, 0xc>(v, v));
+  return readlane_f64(v, 63);
 }
 __device__ __forceinline__ double dpp_wave_sum_f64(double v) {
-  v += dpp_f64<0xB1>(v);
-  v += dpp_f64<0x4E>(v);
-  v += dpp_f64<0x141>(v);
-  v += dpp_f64<0x140>(v);
-  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+  v += dpp_f64<DPP_XOR1, 0xf>(0.0, v);
+  v += dpp_f64<DPP_XOR2, 0xf>(0.0, v);
+  v += dpp_f64<DPP_HALF_MIRROR, 0xf>(0.0, v);
+  v += dpp_f64<DPP_MIRROR, 0xf>(0.0, v);
+  v += dpp_f64<DPP_BCAST15, 0xa>(0.0, v);  // rows outside the mask add 0
+  v += dpp_f64<DPP_BCAST31, 0xc>(0.0, v);
+  return readlane_f64(v, 63);
 }
 
-template <int S, bool BF16>
-__global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ logits, const double *__restrict__ un2,
-                                                   const double *__restrict__ wn, const float *__restrict__ bias,
-                                                   const void *__restrict__ u, const void *__restrict__ w,
-                                                   int64_t T, int E, int d, int k, double c1, int G,
-                                                   int topk_group, int32_t *__restrict__ idx_out,
-                                                   float *__restrict__ w_out, DiagWords *diag) {
+struct TopkArgs {
+  const double *logits, *un2, *wn;
+  const float *bias;
+  const void *u, *w;
+  int64_t T;
+  int E, d, k;
+  double c1;           // first-level bound coefficient (router.hip)
+  int G, topk_group;   // group size (0: not group-limited) and groups kept
+  int32_t *idx_out;
+  float *w_out;
+  DiagWords *diag;
+  int32_t *list;       // tokens left to the cooperative kernel
+};
+
+// A token's state (expert e lives in lane e % 64, register slot e / 64): its
+// logit L, the interval [lo, hi] = [L - B, L + B] around it (both -inf once
+// the expert has left the candidates, and for slots past N_r), the round
+// that took it (rank, -1 if none), the softmax statistics and the groups
+// met so far.
+template <int S>
+struct TokenState {
+  double L[S], lo[S], hi[S];
+  int rank[S];
+  double mx, sum, su;
+  unsigned long long kept;
+  int nkept;
+};
+
+template <int S>
+__device__ __forceinline__ void token_setup(const TopkArgs &a, int64_t t, TokenState<S> &z) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * TOPK_TOKENS_PER_WG + (threadIdx.x >> 6);
-  if (t >= T) return;
-  double L[S], B[S];
-  unsigned avail = 0;
-  const double unorm = un2[t];
-  const double su = sqrt(unorm);  // ||u_t||; wn[e] = ||c_e|| (the (1 + 2^-30) factor covers their rounding)
   const double NEG = -__builtin_huge_val();
+  z.kept = 0;
+  z.nkept = 0;
+  // every load issued before any is used (indices clamped into the rows)
+  double lg[S], cn[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const int e = lane + 64 * s;
-    if (e < E) {
-      L[s] = logits[t * E + e];
-      B[s] = c1 * su * wn[e] * (1.0 + 0x1p-30) + 0x1p-50 * fabs(L[s]) + d * 0x1p-120;
-      avail |= 1u << s;
+    const int e = min(lane + 64 * s, a.E - 1);
+    lg[s] = a.logits[t * a.E + e];
+    cn[s] = a.wn[e];
+  }
+  z.su = sqrt(a.un2[t]);  // ||u_t||; wn[e] = ||c_e|| (the (1 + 2^-30) factor covers their rounding)
+  double mx = NEG;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    z.rank[s] = -1;
+    if (lane + 64 * s < a.E) {
+      const double B = a.c1 * z.su * cn[s] * (1.0 + 0x1p-30) + 0x1p-50 * fabs(lg[s]) + a.d * 0x1p-120;
+      z.L[s] = lg[s];
+      z.lo[s] = lg[s] - B;
+      z.hi[s] = lg[s] + B;
+      mx = fmax(mx, lg[s]);
     } else {
-      L[s] = NEG;
-      B[s] = 0.0;
+      z.L[s] = z.lo[s] = z.hi[s] = NEG;
     }
   }
   // softmax statistics over all experts (fp64)
-  double mx = NEG;
-#pragma unroll
-  for (int s = 0; s < S; ++s) mx = fmax(mx, L[s]);
-  mx = dpp_wave_max_f64(mx);
+  z.mx = dpp_wave_max_f64(mx);
   double sum = 0.0;
 #pragma unroll
   for (int s = 0; s < S; ++s)
-    if (avail & (1u << s)) sum += (double)expf((float)(L[s] - mx));
-  sum = dpp_wave_sum_f64(sum);
+    if (lane + 64 * s < a.E) sum += (double)expf((float)(z.L[s] - z.mx));
+  z.sum = dpp_wave_sum_f64(sum);
+}
 
-  const void *urow = BF16 ? (const void *)((const uint16_t *)u + t * d) : (const void *)((const float *)u + t * d);
-  bool token_exact = false;
-  unsigned bad = 0;
-  int eu = -100000;  // max exponent of |u_t,i|, computed on first need
+// The round's members, the candidates whose interval reaches the largest
+// lower bound, as this lane's slot bits; the winner (uniform) when there is
+// a single member, else -1.  One ballot per slot: the count and the winner
+// come out of the scalar unit.
+template <int S>
+__device__ __forceinline__ int round_members(const TokenState<S> &z, unsigned &member) {
+  double m = z.lo[0];
+#pragma unroll
+  for (int s = 1; s < S; ++s) m = fmax(m, z.lo[s]);
+  m = dpp_wave_max_f64(m);
+  unsigned long long bal[S];
+  int cnt = 0;
+  member = 0;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const bool in = z.hi[s] >= m;
+    bal[s] = __ballot(in);
+    member |= in ? 1u << s : 0u;
+    cnt += __popcll(bal[s]);
+  }
+  if (cnt != 1) return -1;
+  int win = -1;
+#pragma unroll
+  for (int s = S - 1; s >= 0; --s)
+    if (bal[s]) win = (__ffsll((long long)bal[s]) - 1) + 64 * s;
+  return win;
+}
+
+// Round j's winner leaves the candidates; with group limits, its group is
+// kept (it is one of the first topk_group met) and once topk_group groups are
+// met every other group's experts leave too.
+template <int S>
+__device__ __forceinline__ void take_winner(const TopkArgs &a, TokenState<S> &z, int j, int win) {
+  const int lane = threadIdx.x & 63;
+  const double NEG = -__builtin_huge_val();
+  if (a.G > 0) {
+    const int g = win / a.G;
+    if (!((z.kept >> g) & 1ull)) {
+      z.kept |= 1ull << g;
+      if (++z.nkept == a.topk_group) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          const int e = lane + 64 * s;
+          if (e < a.E && !((z.kept >> (e / a.G)) & 1ull)) z.lo[s] = z.hi[s] = NEG;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    if (s == (win >> 6) && lane == (win & 63)) {
+      z.lo[s] = z.hi[s] = NEG;
+      z.rank[s] = j;
+    }
+}
+
+// Every taken expert's lane writes its slot: the index and the full-softmax
+// probability (of its logit as it stands, fp64 where refined).
+template <int S>
+__device__ __forceinline__ void emit_slots(const TopkArgs &a, const TokenState<S> &z, int64_t t) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    if (z.rank[s] >= 0) {
+      a.idx_out[t * a.k + z.rank[s]] = lane + 64 * s;
+      a.w_out[t * a.k + z.rank[s]] = (float)((double)expf((float)(z.L[s] - z.mx)) / z.sum);
+    }
+}
+
+// Level 2 for the members in need (this lane's slot bits): their fp64 logits,
+// lowest index first, M per pass, written back in place with the tighter
+// fp64 bound.  Marks them in refined.
+template <int S, bool BF16, int NW, int M, int DB>
+__device__ __forceinline__ void refine_members(const TopkArgs &a, TokenState<S> &z, const void *urow, unsigned need,
+                                               unsigned &refined, double (*part)[M]) {
+  const int lane = threadIdx.x & 63;
+  const int d = a.d;
   const double c64 = (d / 64 + 8) * 0x1p-52;  // fp64 refinement bound coefficient
-  unsigned refined = 0;                         // slots whose L/B hold fp64 values
-  unsigned long long kept = 0;                  // groups met so far (G > 0)
-  int nkept = 0;
-  for (int j = 0; j < k; ++j) {
-    int win = -1;
+  for (;;) {
+    int es[M];
+    int m = 0;
+#pragma unroll
+    for (int q = 0; q < M; ++q) {
+      es[q] = lowest_expert<S>(need);
+      if (es[q] != 0x7fffffff) {
+        if ((es[q] & 63) == lane) need &= ~(1u << (es[q] >> 6));
+        ++m;
+      }
+    }
+    if (m == 0) break;
+    double l64[M];
+    coop_dots<BF16, NW, M, DB>(urow, a.w, a.bias, es, m, d, part, l64);
+    for (int q = 0; q < M; ++q) {
+      const int e = es[q];
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+        if (q < m && e == lane + 64 * s) {
+          const double b64 = c64 * z.su * a.wn[e] * (1.0 + 0x1p-30) + 0x1p-51 * fabs(l64[q]) + d * 0x1p-120;
+          z.L[s] = l64[q];
+          z.lo[s] = l64[q] - b64;
+          z.hi[s] = l64[q] + b64;
+          refined |= 1u << s;
+        }
+    }
+  }
+}
+
+// Level 3: the exact tournament over the members (this lane's slot bits), in
+// ascending expert order, ties to the lower index; returns the winner
+// (uniform).  eu caches the largest exponent of the token's elements.  Kept
+// out of line: it is rare, and its fixed-point registers would otherwise
+// count against the occupancy of the common path.
+template <int S, bool BF16>
+__device__ __attribute__((noinline)) int exact_tournament(const void *urow, const void *w, const float *bias,
+                                                          unsigned member, int d, int &eu, unsigned &bad) {
+  const int lane = threadIdx.x & 63;
+  if (eu == -100000) {
+    int mm = -100000;
+    for (int i = lane; i < d; i += 64) mm = max(mm, exponent_of(load_elem<BF16>(urow, i)));
+    eu = wave_max_i32(mm);
+  }
+  int ew = -100000, eb = -100000;
+  for (unsigned rest = member;;) {
+    const int e = lowest_expert<S>(rest);
+    if (e == 0x7fffffff) break;
+    for (int i = lane; i < d; i += 64) ew = max(ew, exponent_of(load_elem<BF16>(w, (int64_t)e * d + i)));
+    if (bias) eb = max(eb, exponent_of((double)bias[e]));
+    if ((e & 63) == lane) rest &= ~(1u << (e >> 6));
+  }
+  ew = wave_max_i32(ew);
+  eb = __builtin_amdgcn_readfirstlane(eb);
+  int lg = 1;
+  while ((1 << lg) < d + 2) ++lg;
+  const int top = max(eu + ew + 2, eb + 1) + lg + 1;
+  const int E0 = __builtin_amdgcn_readfirstlane(top - 240);
+  long long best[EXACT_LIMBS];
+  long long cur[EXACT_LIMBS];
+  int exact_win = -1;
+#pragma unroll
+  for (int q = 0; q < EXACT_LIMBS; ++q) best[q] = 0;
+  for (unsigned rest = member;;) {  // ascending expert order
+    const int e = lowest_expert<S>(rest);
+    if (e == 0x7fffffff) break;
+    if ((e & 63) == lane) rest &= ~(1u << (e >> 6));
+    exact_key<BF16>(urow, w, bias, e, d, E0, cur, bad);
+    // keys are wave sums: make their uniformity explicit before comparing
+    int better = 0;
+    if (exact_win >= 0) better = exact_cmp(cur, best) > 0 ? 1 : 0;
+    better = __builtin_amdgcn_readfirstlane(better);
+    if (exact_win < 0 || better) {
+      exact_win = e;
+#pragma unroll
+      for (int q = 0; q < EXACT_LIMBS; ++q) best[q] = cur[q];
+    }
+  }
+  return __builtin_amdgcn_readfirstlane(exact_win);
+}
+
+// First kernel: one wavefront per token, levels 1 and 2.  A token whose
+// rounds all settle with fp64 refinement at most is finished here (its
+// diagnostics counted here); a round that needs the exact level sends the
+// token to the list, and the second kernel takes it from the start.
+template <int S, bool BF16>
+__global__ __launch_bounds__(256) void topk_fast_kernel(TopkArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * TOPK_TOKENS_PER_WG + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  TokenState<S> z;
+  token_setup<S>(a, t, z);
+  const void *urow = BF16 ? (const void *)((const uint16_t *)a.u + t * a.d) : (const void *)((const float *)a.u + t * a.d);
+  unsigned refined = 0, passes = 0;
+  for (int j = 0; j < a.k; ++j) {
+    int win;
     for (;;) {
-      double mlo = NEG;
-#pragma unroll
-      for (int s = 0; s < S; ++s)
-        if (avail & (1u << s)) mlo = fmax(mlo, L[s] - B[s]);
-      mlo = dpp_wave_max_f64(mlo);
-      unsigned member = 0;
-#pragma unroll
-      for (int s = 0; s < S; ++s)
-        if ((avail & (1u << s)) && L[s] + B[s] >= mlo) member |= 1u << s;
-      const int mine = __popc(member);
-      const unsigned long long holders = __ballot(mine > 0);
-      if (__popcll(holders) == 1 && __ballot(mine > 1) == 0) {
-        // a single member: the one lane holding one, in its lowest set slot
-        const int my = member ? lane + 64 * (__ffs(member) - 1) : 0;
-        win = __builtin_amdgcn_readlane(my, __ffsll((long long)holders) - 1);
+      unsigned member;
+      win = round_members<S>(z, member);
+      if (win >= 0) break;
+      const unsigned need = member & ~refined;
+      if (!__ballot(need != 0u)) {  // the exact level: left to the second kernel
+        if (lane == 0) a.list[atomicAdd(&a.diag->deferred, 1u)] = (int32_t)t;
+        return;
+      }
+      refine_members<S, BF16, 1, TOPK_MEMBERS_1, TOPK_FAST_BATCH>(a, z, urow, need, refined, nullptr);
+      ++passes;
+    }
+    take_winner<S>(a, z, j, win);
+  }
+  emit_slots<S>(a, z, t);
+  if (lane == 0 && passes) {
+    atomicAdd(&a.diag->tokens_exact, 1u);
+    atomicAdd(&a.diag->refinements, passes);
+  }
+}
+
+// Second kernel: the full procedure for the listed tokens (LIST) or for
+// tokens 0 .. T - 1, with NW wavefronts per token: one (four tokens per
+// work-group, each wave on its own) or four.  Four waves load the same
+// logits and take the same decisions, so their control flow agrees and they
+// meet at every barrier; fp64 refinements split the work over the four
+// (coop_dots), the exact level runs in each wave, and wave 0 writes the slots
+// and diagnostics.
+template <int S, bool BF16, bool LIST, int NW>
+__global__ __launch_bounds__(256) void topk_coop_kernel(TopkArgs a) {
+  constexpr int M = NW == 1 ? TOPK_MEMBERS_1 : TOPK_MEMBERS_4;  // members per refinement pass
+  __shared__ double part[4][M];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const bool lead = NW == 1 || wv == 0;  // writes the slots and diagnostics
+  const int64_t n = LIST ? (int64_t)(*(volatile const uint32_t *)&a.diag->deferred) : a.T;
+  const int d = a.d;
+  const int per = 4 / NW;                     // tokens per work-group
+  for (int64_t i = (int64_t)blockIdx.x * per + (NW == 1 ? wv : 0); i < n; i += (int64_t)gridDim.x * per) {
+    const int64_t t = LIST ? (int64_t)a.list[i] : i;
+    TokenState<S> z;
+    token_setup<S>(a, t, z);
+    const void *urow = BF16 ? (const void *)((const uint16_t *)a.u + t * d) : (const void *)((const float *)a.u + t * d);
+    bool token_exact = false;
+    unsigned bad = 0;
+    int eu = -100000;     // max exponent of |u_t,i|, computed on first need
+    unsigned refined = 0;  // slots whose L/B hold fp64 values
+    for (int j = 0; j < a.k; ++j) {
+      int win = -1;
+      for (;;) {
+        unsigned member;
+        win = round_members<S>(z, member);
+        if (win >= 0) break;
+        token_exact = true;
+        unsigned need = member & ~refined;
+        if (__ballot(need != 0u)) {
+          // level 2
+          refine_members<S, BF16, NW, M, TOPK_DOT_BATCH>(a, z, urow, need, refined, part);
+          if (lead && lane == 0) atomicAdd(&a.diag->refinements, 1u);
+          continue;  // re-decide the round with the tighter intervals
+        }
+        // level 3: exact tournament over the (all refined) members
+        win = exact_tournament<S, BF16>(urow, a.w, a.bias, member, d, eu, bad);
+        const int cnt = wave_sum_i32(__popc(member));
+        if (lead && lane == 0) atomicAdd(&a.diag->exact_keys, (unsigned)cnt);
         break;
       }
-      token_exact = true;
-      unsigned need = member & ~refined;
-      if (__ballot(need != 0u)) {
-        // level 2: fp64 logits of the unrefined members, written back in place
-        // (expert e lives in lane e % 64, register slot e / 64)
-        for (int e = lowest_expert<S>(need); e != 0x7fffffff; e = lowest_expert<S>(need)) {
-          const double l64 = dot_f64<BF16>(urow, w, bias, e, d);
-          const double b64 = c64 * su * wn[e] * (1.0 + 0x1p-30) + 0x1p-51 * fabs(l64) + d * 0x1p-120;
-#pragma unroll
-          for (int s = 0; s < S; ++s)
-            if (lane + 64 * s == e) {
-              L[s] = l64;
-              B[s] = b64;
-              refined |= 1u << s;
-              need &= ~(1u << s);
-            }
-        }
-        if (lane == 0) atomicAdd(&diag->refinements, 1u);
-        continue;  // re-decide the round with the tighter intervals
-      }
-      // level 3: exact tournament over the (all refined) members, ascending index
-      if (eu == -100000) {
-        int m = -100000;
-        for (int i = lane; i < d; i += 64) m = max(m, exponent_of(load_elem<BF16>(urow, i)));
-        eu = wave_max_i32(m);
-      }
-      int ew = -100000, eb = -100000;
-      for (unsigned rest = member; ; ) {
-        const int e = lowest_expert<S>(rest);
-        if (e == 0x7fffffff) break;
-        for (int i = lane; i < d; i += 64) ew = max(ew, exponent_of(load_elem<BF16>(w, (int64_t)e * d + i)));
-        if (bias) eb = max(eb, exponent_of((double)bias[e]));
-        if ((e & 63) == lane) rest &= ~(1u << (e >> 6));
-      }
-      ew = wave_max_i32(ew);
-      eb = __builtin_amdgcn_readfirstlane(eb);
-      int lg = 1;
-      while ((1 << lg) < d + 2) ++lg;
-      const int top = max(eu + ew + 2, eb + 1) + lg + 1;
-      const int E0 = __builtin_amdgcn_readfirstlane(top - 240);
-      long long best[EXACT_LIMBS];
-      long long cur[EXACT_LIMBS];
-      int exact_win = -1;
-#pragma unroll
-      for (int q = 0; q < EXACT_LIMBS; ++q) best[q] = 0;
-      for (unsigned rest = member; ; ) {  // ascending expert order
-        const int e = lowest_expert<S>(rest);
-        if (e == 0x7fffffff) break;
-        if ((e & 63) == lane) rest &= ~(1u << (e >> 6));
-        exact_key<BF16>(urow, w, bias, e, d, E0, cur, bad);
-        // keys are wave sums: make their uniformity explicit before comparing
-        int better = 0;
-        if (exact_win >= 0) better = exact_cmp(cur, best) > 0 ? 1 : 0;
-        better = __builtin_amdgcn_readfirstlane(better);
-        if (exact_win < 0 || better) {
-          exact_win = e;
-#pragma unroll
-          for (int q = 0; q < EXACT_LIMBS; ++q) best[q] = cur[q];
-        }
-      }
-      win = __builtin_amdgcn_readfirstlane(exact_win);
-      const int cnt = wave_sum_i32(mine);
-      if (lane == 0) atomicAdd(&diag->exact_keys, (unsigned)cnt);
-      break;
+      take_winner<S>(a, z, j, win);
     }
-    if (G > 0) {  // group-limited: the winner's group is kept (it is one of the first topk_group met)
-      const int g = win / G;
-      if (!((kept >> g) & 1ull)) {
-        kept |= 1ull << g;
-        if (++nkept == topk_group) {
-#pragma unroll
-          for (int s = 0; s < S; ++s) {
-            const int e = lane + 64 * s;
-            if (e < E && !((kept >> (e / G)) & 1ull)) avail &= ~(1u << s);
-          }
-        }
-      }
-    }
-    // the winner's lane takes it out and emits its slot
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-      if (lane + 64 * s == win) {
-        avail &= ~(1u << s);
-        idx_out[t * k + j] = win;
-        w_out[t * k + j] = (float)((double)expf((float)(L[s] - mx)) / sum);
-      }
+    if (lead) emit_slots<S>(a, z, t);
+    if (lead && lane == 0 && token_exact) atomicAdd(&a.diag->tokens_exact, 1u);
+    if (__ballot(bad != 0u) && lead && lane == 0) atomicOr(&a.diag->flags, MOE_DIAG_UNRESOLVED);
   }
-  if (lane == 0) {
-    if (token_exact) atomicAdd(&diag->tokens_exact, 1u);
+}
+
+template <int S, bool BF16>
+static void launch_topk_s(const moe_dims &dm, int64_t T, const void *u, const void *w, const float *bias,
+                          int32_t *idx, float *wout, const WsLayout &L, char *ws, hipStream_t st) {
+  // group size, or 0 when routing is not group-limited
+  const bool grouped = dm.n_group > 1 && dm.topk_group < dm.n_group;
+  TopkArgs a{(const double *)(ws + L.logits), (const double *)(ws + L.unorm2), (const double *)(ws + L.wnorm),
+             bias, u, w, T, dm.n_routed, dm.d_model, dm.top_k, router_bound_coeff(dm),
+             grouped ? dm.n_routed / dm.n_group : 0, dm.topk_group, idx, wout, (DiagWords *)(ws + L.diag),
+             (int32_t *)(ws + L.topk_list)};
+  if (T <= MOE_TOPK_COOP_ALL) {
+    topk_coop_kernel<S, BF16, false, 4><<<dim3((unsigned)T), 256, 0, st>>>(a);
+    return;
   }
-  if (__ballot(bad != 0u) && lane == 0) atomicOr(&diag->flags, MOE_DIAG_UNRESOLVED);
+  const int64_t wgs = (T + TOPK_TOKENS_PER_WG - 1) / TOPK_TOKENS_PER_WG;
+  topk_fast_kernel<S, BF16><<<dim3((unsigned)wgs), 256, 0, st>>>(a);
+  topk_coop_kernel<S, BF16, true, 4><<<dim3((unsigned)TOPK_LIST_WGS), 256, 0, st>>>(a);
 }
 
 template <int S>
-static void launch_topk_s(const moe_dims &dm, int64_t T, const void *u, const void *w, const float *bias,
-                          int32_t *idx, float *wout, const WsLayout &L, char *ws, hipStream_t st) {
-  const double c1 = router_bound_coeff(dm);
-  dim3 grid((unsigned)((T + TOPK_TOKENS_PER_WG - 1) / TOPK_TOKENS_PER_WG));
-  const double *lg = (const double *)(ws + L.logits);
-  const double *un2 = (const double *)(ws + L.unorm2);
-  const double *wn = (const double *)(ws + L.wnorm);
-  DiagWords *diag = (DiagWords *)(ws + L.diag);
-  // group size, or 0 when routing is not group-limited
-  const bool grouped = dm.n_group > 1 && dm.topk_group < dm.n_group;
-  const int G = grouped ? dm.n_routed / dm.n_group : 0;
-  if (dm.dtype == MOE_BF16)
-    topk_kernel<S, true><<<grid, 256, 0, st>>>(lg, un2, wn, bias, u, w, T, dm.n_routed, dm.d_model, dm.top_k, c1,
-                                               G, dm.topk_group, idx, wout, diag);
-  else
-    topk_kernel<S, false><<<grid, 256, 0, st>>>(lg, un2, wn, bias, u, w, T, dm.n_routed, dm.d_model, dm.top_k, c1,
-                                                G, dm.topk_group, idx, wout, diag);
+static void launch_topk_dt(const moe_dims &dm, int64_t T, const void *u, const void *w, const float *bias,
+                           int32_t *idx, float *wout, const WsLayout &L, char *ws, hipStream_t st) {
+  if (dm.dtype == MOE_BF16) launch_topk_s<S, true>(dm, T, u, w, bias, idx, wout, L, ws, st);
+  else launch_topk_s<S, false>(dm, T, u, w, bias, idx, wout, L, ws, st);
 }
 
 hipError_t launch_topk(const moe_dims &dm, int64_t T, const void *u, const void *w_router, const float *bias,
                        int32_t *topk_idx, float *topk_w, const WsLayout &L, char *ws, hipStream_t st) {
   const int E = dm.n_routed;
-  if (E <= 64) launch_topk_s<1>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
-  else if (E <= 128) launch_topk_s<2>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
-  else if (E <= 256) launch_topk_s<4>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
-  else if (E <= 512) launch_topk_s<8>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
-  else launch_topk_s<16>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
+  if (E <= 64) launch_topk_dt<1>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
+  else if (E <= 128) launch_topk_dt<2>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
+  else if (E <= 256) launch_topk_dt<4>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
+  else if (E <= 512) launch_topk_dt<8>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
+  else launch_topk_dt<16>(dm, T, u, w_router, bias, topk_idx, topk_w, L, ws, st);
   return hipGetLastError();
 }
 
@@ -402,6 +616,7 @@ __global__ void diag_clear_kernel(DiagWords *d) {
     d->tokens_exact = 0;
     d->exact_keys = 0;
     d->refinements = 0;
+    d->deferred = 0;
   }
 }
 
