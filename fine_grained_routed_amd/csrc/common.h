@@ -166,6 +166,7 @@ struct WsLayout {
   size_t diag;        // DiagWords
   size_t logits;      // double [T, N_r]
   size_t logit_part;  // double [S, T, N_r] router partial sums (S = router_splits > 1 only)
+  size_t norm_part;   // double [S, T] then [S, N_r]: the slices' partial squared norms (S > 1 only)
   size_t unorm2;      // double [T]   squared 2-norm of each token row
   size_t wnorm;       // double [N_r] 2-norm of each router row
   size_t blk;         // int32  [nblk, N_r] per-block histograms, then bases
@@ -246,6 +247,7 @@ static inline WsLayout moe_ws_layout(const moe_dims &dm, int64_t T) {
   L.logits = take((size_t)T * E * 8);
   const int S = router_splits(dm, T);
   L.logit_part = take(S > 1 ? (size_t)S * T * E * 8 : 0);
+  L.norm_part = take(S > 1 ? (size_t)S * ((size_t)T + E) * 8 : 0);
   L.unorm2 = take((size_t)T * 8);
   L.wnorm = take(E * 8);
   L.blk = take(nblk * E * 4);
@@ -282,8 +284,9 @@ static inline WsLayout moe_ws_layout(const moe_dims &dm, int64_t T) {
 // Implemented in the per-stage sources; all enqueue on `st` and return the
 // launch status.
 hipError_t launch_diag_clear(void *ws, hipStream_t st);
+// clear_diag: the first kernel also zeroes the diagnostics header (saving a launch).
 hipError_t launch_router_logits(const moe_dims &dm, int64_t T, const void *u, const void *w_router,
-                                const float *bias, const WsLayout &L, char *ws, hipStream_t st);
+                                const float *bias, const WsLayout &L, char *ws, bool clear_diag, hipStream_t st);
 hipError_t launch_topk(const moe_dims &dm, int64_t T, const void *u, const void *w_router, const float *bias,
                        int32_t *topk_idx, float *topk_w, const WsLayout &L, char *ws, hipStream_t st);
 hipError_t launch_permute(const moe_dims &dm, int64_t T, const int32_t *topk_idx, int32_t *counts,

@@ -240,9 +240,9 @@ static moe_status run_layer(const moe_dims &dm, int64_t T, const void *u, const 
   int32_t *token_row = (int32_t *)(w + L.token_row);
   float *y_rows = (float *)(w + L.y_rows);
   float *y_sh = dm.d_ff_shared > 0 ? (float *)(w + L.y_sh) : nullptr;
-  MOE_TRY_HIP(launch_diag_clear(w, st), "diag clear");
-  if (dm.n_routed > 0) {
-    MOE_TRY_HIP(launch_router_logits(dm, T, u, wts.w_router, wts.router_bias, L, w, st), "router logits");
+  if (dm.n_routed == 0) MOE_TRY_HIP(launch_diag_clear(w, st), "diag clear");
+  if (dm.n_routed > 0) {  // the router's first kernel clears the diagnostics
+    MOE_TRY_HIP(launch_router_logits(dm, T, u, wts.w_router, wts.router_bias, L, w, true, st), "router logits");
     ev.rec(1);
     MOE_TRY_HIP(launch_topk(dm, T, u, wts.w_router, wts.router_bias, idx, gw, L, w, st), "top-k");
     ev.rec(2);
@@ -324,8 +324,7 @@ moe_status moe_router_topk(const moe_dims *dims, int64_t T, const void *u, const
   MOE_CHECK(check_ws(*dims, T, ws, ws_bytes, &L));
   hipStream_t st = (hipStream_t)stream;
   char *w = (char *)ws;
-  MOE_TRY_HIP(launch_diag_clear(w, st), "diag clear");
-  MOE_TRY_HIP(launch_router_logits(*dims, T, u, w_router, router_bias, L, w, st), "router logits");
+  MOE_TRY_HIP(launch_router_logits(*dims, T, u, w_router, router_bias, L, w, true, st), "router logits");
   MOE_TRY_HIP(launch_topk(*dims, T, u, w_router, router_bias, topk_idx, topk_w, L, w, st), "top-k");
   return MOE_OK;
 }

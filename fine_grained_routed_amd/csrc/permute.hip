@@ -56,22 +56,49 @@ __global__ __launch_bounds__(MOE_PERM_BLOCK) void perm_hist_kernel(const int32_t
   }
 }
 
-// Exclusive scan of v over the work-group (blockDim.x == 1024), returns the
-// exclusive prefix of this thread and writes the total to *total.
-__device__ int block_exclusive_scan(int v, int *sh, int *total) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
+// Exclusive scans of the N values v[n] over the work-group (blockDim.x a
+// multiple of 64, at most 1024): excl[n] is this thread's prefix, total[n]
+// the sum.  Each wave scans in registers (shuffles), the wave totals meet in
+// LDS (sh: 16 N ints) behind one barrier, and a second barrier frees sh.
+// Integer sums: the result does not depend on the order.
+template <int N>
+__device__ __forceinline__ void block_scan_n(const int (&v)[N], int (&excl)[N], int (&total)[N], int *sh) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int incl[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) incl[n] = v[n];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1)
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      const int y = __shfl_up(incl[n], o, 64);
+      if (lane >= o) incl[n] += y;
+    }
+  if (lane == 63)
+#pragma unroll
+    for (int n = 0; n < N; ++n) sh[wv * N + n] = incl[n];
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    int add = tid >= o ? sh[tid - o] : 0;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    int pre = 0, tot = 0;
+    for (int w2 = 0; w2 < nw; ++w2) {
+      const int x = sh[w2 * N + n];
+      pre += w2 < wv ? x : 0;
+      tot += x;
+    }
+    excl[n] = pre + incl[n] - v[n];
+    total[n] = tot;
   }
-  const int incl = sh[tid];
-  *total = sh[1023];
   __syncthreads();
-  return incl - v;
+}
+
+// single-value form: returns the exclusive prefix, the total in *total
+__device__ __forceinline__ int block_exclusive_scan(int v, int *sh, int *total) {
+  const int vv[1] = {v};
+  int ex[1], tot[1];
+  block_scan_n<1>(vv, ex, tot, sh);
+  *total = tot[0];
+  return ex[0];
 }
 
 // cap: seats per expert, 0 = no limit
@@ -168,24 +195,27 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
     for (int q = 0; q < PERM_WORDS; ++q) tot += __popcll(bm[tid * PERM_WORDS + q]);
   }
   const int seats = (cap > 0 && tot > cap) ? cap : tot;
-  int all;
-  const int off = block_exclusive_scan(tid < E ? seats : 0, sh, &all);
+  // one scan for the row offsets and every tile height's m-tile prefixes
+  int v[1 + MOE_N_BM], ex[1 + MOE_N_BM], all[1 + MOE_N_BM];
+  v[0] = tid < E ? seats : 0;
+#pragma unroll
+  for (int b = 0; b < MOE_N_BM; ++b) v[1 + b] = tid < E ? (seats + moe_bm_of(b) - 1) / moe_bm_of(b) : 0;
+  block_scan_n<1 + MOE_N_BM>(v, ex, all, sh);
   if (tid < E) {
     counts[tid] = seats;
-    offsets[tid] = off;
-    start[tid] = off;
+    offsets[tid] = ex[0];
+    start[tid] = ex[0];
   }
-  if (tid == 0) offsets[E] = all;
+  if (tid == 0) offsets[E] = all[0];
   if (tile_off) {
+#pragma unroll
     for (int b = 0; b < MOE_N_BM; ++b) {
       const int bmh = moe_bm_of(b);
-      int tiles;
-      const int toff = block_exclusive_scan(tid < E ? (seats + bmh - 1) / bmh : 0, sh, &tiles);
       int32_t *to = tile_off + b * (E + 2);
-      if (tid < E) to[tid] = toff;
+      if (tid < E) to[tid] = ex[1 + b];
       if (tid == 0) {
-        to[E] = tiles;
-        to[E + 1] = tiles + (has_shared ? (int)((T + bmh - 1) / bmh) : 0);
+        to[E] = all[1 + b];
+        to[E + 1] = all[1 + b] + (has_shared ? (int)((T + bmh - 1) / bmh) : 0);
       }
     }
   }
@@ -251,15 +281,18 @@ __global__ __launch_bounds__(1024) void tile_offsets_kernel(const int32_t *__res
   __shared__ int sh[1024];
   const int e = threadIdx.x;
   const int c = e < E ? counts[e] : 0;
+  int v[MOE_N_BM], ex[MOE_N_BM], all[MOE_N_BM];
+#pragma unroll
+  for (int b = 0; b < MOE_N_BM; ++b) v[b] = e < E ? (c + moe_bm_of(b) - 1) / moe_bm_of(b) : 0;
+  block_scan_n<MOE_N_BM>(v, ex, all, sh);
+#pragma unroll
   for (int b = 0; b < MOE_N_BM; ++b) {
     const int bm = moe_bm_of(b);
-    int all;
-    const int off = block_exclusive_scan(e < E ? (c + bm - 1) / bm : 0, sh, &all);
     int32_t *to = tile_off + b * (E + 2);
-    if (e < E) to[e] = off;
+    if (e < E) to[e] = ex[b];
     if (e == 0) {
-      to[E] = all;
-      to[E + 1] = all + (has_shared ? (int)((T + bm - 1) / bm) : 0);
+      to[E] = all[b];
+      to[E + 1] = all[b] + (has_shared ? (int)((T + bm - 1) / bm) : 0);
     }
   }
 }

@@ -26,36 +26,17 @@
 #define RT_BK 64
 #define RT_LDS_STRIDE (RT_BK + 8)  // bf16 elements per LDS row (16-byte pad)
 
-// ------------------------------------------------------------------ row norms
-// out[r] = sum_i x[r,i]^2 in fp64 (one wave per row), or its square root (ROOT).
-template <bool BF16, bool ROOT = false>
-__global__ __launch_bounds__(256) void row_norm2_kernel(const void *__restrict__ x, int64_t rows, int d,
-                                                        double *__restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
+// sum of the squares of 8 bf16 values, in fp64 (each square exact)
+__device__ __forceinline__ double sumsq_bf16x8(const uint4 &v) {
+  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
   double s = 0.0;
-  if (BF16) {
-    const uint16_t *p = (const uint16_t *)x + r * d;
-    for (int i = lane * 8; i < d; i += 512) {
-      uint4 v = *(const uint4 *)(p + i);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        double a = (double)__uint_as_float(w4[q] << 16);
-        double b = (double)__uint_as_float(w4[q] & 0xffff0000u);
-        s += a * a + b * b;
-      }
-    }
-  } else {
-    const float *p = (const float *)x + r * d;
-    for (int i = lane; i < d; i += 64) {
-      double a = (double)p[i];
-      s += a * a;
-    }
+  for (int q = 0; q < 4; ++q) {
+    const double lo = (double)__uint_as_float(w4[q] << 16), hi = (double)__uint_as_float(w4[q] & 0xffff0000u);
+    s = fma(lo, lo, s);
+    s = fma(hi, hi, s);
   }
-  s = wave_sum_f64(s);
-  if (lane == 0) out[r] = ROOT ? sqrt(s) : s;
+  return s;
 }
 
 // -------------------------------------------------------- bf16 logits (MFMA)
@@ -63,11 +44,19 @@ __global__ __launch_bounds__(256) void row_norm2_kernel(const void *__restrict__
 // 32 x 32 = 2 x 2 MFMA 16x16x32 tiles.
 // blockIdx.z selects a slice of kps k-tiles; with one slice the logits (bias
 // added) are written, otherwise slice s writes its fp64 partial sums to
-// logits + s * T * E and router_reduce_kernel adds them.
+// logits + s * T * E and router_reduce_kernel adds them.  The squared norms
+// come out of the same loads: work-groups of the first expert tile sum their
+// token rows' squares, those of the first token tile their router rows'; with
+// one slice they write ||u_t||^2 to un2 and ||c_e|| to cn, otherwise slice s
+// writes its partial sums to un2 + s * T and cn + s * E for the reduction.
+// clear (or NULL): the diagnostics header, zeroed by the first work-group.
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const uint16_t *__restrict__ u,
                                                                  const uint16_t *__restrict__ w,
                                                                  const float *__restrict__ bias, int64_t T,
-                                                                 int E, int d, int kps, double *__restrict__ logits) {
+                                                                 int E, int d, int kps, double *__restrict__ logits,
+                                                                 double *__restrict__ un2, double *__restrict__ cn,
+                                                                 DiagWords *clear) {
+  if (clear && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *clear = DiagWords{};
   __shared__ __attribute__((aligned(16))) uint16_t As[RT_BM * RT_LDS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[RT_BN * RT_LDS_STRIDE];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -111,12 +100,16 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const uint16_t 
     av[q] = keep_or_zero(aok[q], *(const uint4 *)(ap[q] + kt0 * RT_BK));  // pointers clamped in bounds
     bv[q] = keep_or_zero(bok[q], *(const uint4 *)(bp[q] + kt0 * RT_BK));
   }
+  const bool unorm = blockIdx.y == 0, cnorm = blockIdx.x == 0;
+  double usq[2] = {0.0, 0.0}, csq[2] = {0.0, 0.0};  // this thread's squares of its two chunk rows
   for (int kt = kt0; kt < kt1; ++kt) {
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       *(uint4 *)&As[lrow[q] * RT_LDS_STRIDE + lcol[q]] = av[q];
       *(uint4 *)&Bs[lrow[q] * RT_LDS_STRIDE + lcol[q]] = bv[q];
+      if (unorm) usq[q] += sumsq_bf16x8(av[q]);
+      if (cnorm) csq[q] += sumsq_bf16x8(bv[q]);
     }
     __syncthreads();
     const int kn = min(kt + 1, kt1 - 1);  // the last trip re-loads its own tile (in bounds, unused)
@@ -152,6 +145,24 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const uint16_t 
         }
     }
   }
+  // norms: the 8 threads of a chunk row are consecutive lanes; their sums
+  // are added in a fixed butterfly order
+  const bool whole = gridDim.z == 1;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    double su = usq[q], sc = csq[q];
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      su += __shfl_xor(su, o, 64);
+      sc += __shfl_xor(sc, o, 64);
+    }
+    if (lcol[q] == 0) {
+      const int64_t t = t0 + lrow[q];
+      const int e = e0 + lrow[q];
+      if (unorm && t < T) un2[(whole ? 0 : (int64_t)blockIdx.z * T) + t] = su;
+      if (cnorm && e < E) cn[(whole ? 0 : (int64_t)blockIdx.z * E) + e] = whole ? sqrt(sc) : sc;
+    }
+  }
   // D layout of a 16x16 tile: lane holds rows 4*(lane/16)+r, column lane%16
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -159,7 +170,6 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(const uint16_t 
     for (int j = 0; j < 2; ++j) {
       const int e = e0 + wn * 32 + j * 16 + (lane & 15);
       if (e >= E) continue;
-      const bool whole = gridDim.z == 1;
       const double b = (whole && bias) ? (double)bias[e] : 0.0;
       double *dst = logits + (whole ? 0 : (int64_t)blockIdx.z * T * E);
 #pragma unroll
@@ -219,6 +229,7 @@ struct RwArgs {
   double *logits;    // [T, E]
   double *unorm2;    // [T] squared token norms
   double *wnorm;     // [E] router row norms
+  DiagWords *clear;  // the diagnostics header, zeroed by the first work-group (or NULL)
 };
 
 // DMA of k-tile kt into stage S: lane l of wave w fills LDS row 8 w + l / 8 of
@@ -323,6 +334,7 @@ __device__ __forceinline__ void rw_loop(const __amdgpu_buffer_rsrc_t &ra, const 
 
 __global__ __launch_bounds__(64 * RW_WAVES, 1) void router_logits_wide_kernel(RwArgs a) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (a.clear && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.clear = DiagWords{};
   const int64_t t0 = (int64_t)blockIdx.x * RW_BM;
   const int e0 = blockIdx.y * RW_BN;
   const int n = a.d / RT_BK;
@@ -402,23 +414,37 @@ __global__ __launch_bounds__(64 * RW_WAVES, 1) void router_logits_wide_kernel(Rw
   }
 }
 
-// logits[t, e] = sum over slices s = 0, 1, ... of part[s][t][e] (in this
-// order) + b_e.
-__global__ __launch_bounds__(256) void router_reduce_kernel(const double *__restrict__ part, int S, int64_t n, int E,
-                                                            const float *__restrict__ bias, double *__restrict__ logits) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  // loads in batches of 8 (in flight together), additions in slice order
+// Sum over slices z = 0, 1, ..., S - 1 (in this order) of p[z * stride + i],
+// the loads in batches of 8 that are in flight together.
+__device__ __forceinline__ double slice_sum(const double *__restrict__ p, int S, int64_t stride, int64_t i) {
   double s = 0.0;
   for (int k0 = 0; k0 < S; k0 += 8) {
     double v[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = k0 + q < S ? part[(int64_t)(k0 + q) * n + i] : 0.0;
+    for (int q = 0; q < 8; ++q) v[q] = k0 + q < S ? p[(int64_t)(k0 + q) * stride + i] : 0.0;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       if (k0 + q < S) s = (k0 + q == 0) ? v[q] : s + v[q];
   }
-  logits[i] = s + (bias ? (double)bias[i % E] : 0.0);
+  return s;
+}
+
+// Thread i < n = T * E: logits[i] = the slices' partial sums of logit i + b_e;
+// the next T threads: un2[t] = the slices' partial squared token norms; the
+// next E: wn[e] = the square root of the slices' partial squared row norms.
+__global__ __launch_bounds__(256) void router_reduce_kernel(const double *__restrict__ part, int S, int64_t n, int E,
+                                                            const float *__restrict__ bias, double *__restrict__ logits,
+                                                            int64_t T, const double *__restrict__ un2p,
+                                                            const double *__restrict__ wnp, double *__restrict__ un2,
+                                                            double *__restrict__ wn) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    logits[i] = slice_sum(part, S, n, i) + (bias ? (double)bias[i % E] : 0.0);
+  } else if (i < n + T) {
+    un2[i - n] = slice_sum(un2p, S, T, i - n);
+  } else if (i < n + T + E) {
+    wn[i - n - T] = sqrt(slice_sum(wnp, S, E, i - n - T));
+  }
 }
 
 // ------------------------------------------------------ fp32 logits (fp64 VALU)
@@ -426,20 +452,34 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const double *__rest
 __global__ __launch_bounds__(256) void router_logits_f32_kernel(const float *__restrict__ u,
                                                                 const float *__restrict__ w,
                                                                 const float *__restrict__ bias, int64_t T,
-                                                                int E, int d, double *__restrict__ logits) {
+                                                                int E, int d, double *__restrict__ logits,
+                                                                double *__restrict__ un2, double *__restrict__ wn,
+                                                                DiagWords *clear) {
   __shared__ float As[16][65];
   __shared__ float Bs[16][65];
+  if (clear && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *clear = DiagWords{};
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 16 + ty;
   const int e = blockIdx.y * 16 + tx;
+  // the squared norms from the same loads: lane l of wave w loads column l of
+  // rows w, w + 4, w + 8, w + 12; the first expert tile's work-groups sum the
+  // token rows, the first token tile's the router rows
+  const bool unorm = blockIdx.y == 0, cnorm = blockIdx.x == 0;
+  double usq[4] = {0.0, 0.0, 0.0, 0.0}, csq[4] = {0.0, 0.0, 0.0, 0.0};
   double acc = 0.0;
   for (int k0 = 0; k0 < d; k0 += 64) {
-    for (int c = threadIdx.x; c < 16 * 64; c += 256) {
-      const int r = c >> 6, col = c & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wv + 4 * i;
       const int64_t tr = (int64_t)blockIdx.x * 16 + r;
       const int er = blockIdx.y * 16 + r;
-      As[r][col] = tr < T ? u[tr * d + k0 + col] : 0.f;
-      Bs[r][col] = er < E ? w[(int64_t)er * d + k0 + col] : 0.f;
+      const float av = tr < T ? u[tr * d + k0 + lane] : 0.f;
+      const float bv = er < E ? w[(int64_t)er * d + k0 + lane] : 0.f;
+      As[r][lane] = av;
+      Bs[r][lane] = bv;
+      if (unorm) usq[i] = fma((double)av, (double)av, usq[i]);
+      if (cnorm) csq[i] = fma((double)bv, (double)bv, csq[i]);
     }
     __syncthreads();
 #pragma unroll 8
@@ -447,14 +487,24 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(const float *__r
     __syncthreads();
   }
   if (t < T && e < E) logits[t * E + e] = acc + (bias ? (double)bias[e] : 0.0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wv + 4 * i;
+    const double su = wave_sum_f64(usq[i]), sc = wave_sum_f64(csq[i]);
+    const int64_t tr = (int64_t)blockIdx.x * 16 + r;
+    const int er = blockIdx.y * 16 + r;
+    if (lane == 0 && unorm && tr < T) un2[tr] = su;
+    if (lane == 0 && cnorm && er < E) wn[er] = sqrt(sc);
+  }
 }
 
 hipError_t launch_router_logits(const moe_dims &dm, int64_t T, const void *u, const void *w_router,
-                                const float *bias, const WsLayout &L, char *ws, hipStream_t st) {
+                                const float *bias, const WsLayout &L, char *ws, bool clear_diag, hipStream_t st) {
   const int E = dm.n_routed, d = dm.d_model;
   double *logits = (double *)(ws + L.logits);
   double *un2 = (double *)(ws + L.unorm2);
   double *wn = (double *)(ws + L.wnorm);
+  DiagWords *clear = clear_diag ? (DiagWords *)(ws + L.diag) : nullptr;
   if (dm.dtype == MOE_BF16) {
     const int nk = d / RT_BK;
     const int S = router_splits(dm, T);
@@ -462,26 +512,28 @@ hipError_t launch_router_logits(const moe_dims &dm, int64_t T, const void *u, co
     const int64_t wide_tiles = ((T + RW_BM - 1) / RW_BM) * ((E + RW_BN - 1) / RW_BN);
     if (E >= RW_MIN_EXPERTS && wide_tiles >= RW_MIN_TILES) {
       // wide tiles fill the chip without split-K; the norms come out of the same kernel
-      RwArgs ra{(const uint16_t *)u, (const uint16_t *)w_router, bias, T, E, d, logits, un2, wn};
+      RwArgs ra{(const uint16_t *)u, (const uint16_t *)w_router, bias, T, E, d, logits, un2, wn, clear};
       dim3 grid((unsigned)((T + RW_BM - 1) / RW_BM), (unsigned)((E + RW_BN - 1) / RW_BN));
       router_logits_wide_kernel<<<grid, 64 * RW_WAVES, 0, st>>>(ra);
       return hipGetLastError();
     }
-    row_norm2_kernel<true><<<dim3((unsigned)((T + 3) / 4)), 256, 0, st>>>(u, T, d, un2);
-    row_norm2_kernel<true, true><<<dim3((unsigned)((E + 3) / 4)), 256, 0, st>>>(w_router, E, d, wn);
     dim3 grid((unsigned)((T + RT_BM - 1) / RT_BM), (unsigned)((E + RT_BN - 1) / RT_BN), (unsigned)S);
-    double *part = S > 1 ? (double *)(ws + L.logit_part) : logits;
-    router_logits_bf16_kernel<<<grid, 256, 0, st>>>((const uint16_t *)u, (const uint16_t *)w_router, bias, T, E, d,
-                                                    kps, part);
-    if (S > 1) {
-      const int64_t n = T * E;
-      router_reduce_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(part, S, n, E, bias, logits);
+    if (S == 1) {
+      router_logits_bf16_kernel<<<grid, 256, 0, st>>>((const uint16_t *)u, (const uint16_t *)w_router, bias, T, E, d,
+                                                      kps, logits, un2, wn, clear);
+    } else {
+      double *part = (double *)(ws + L.logit_part);
+      double *un2p = (double *)(ws + L.norm_part), *wnp = un2p + (size_t)S * T;
+      router_logits_bf16_kernel<<<grid, 256, 0, st>>>((const uint16_t *)u, (const uint16_t *)w_router, bias, T, E, d,
+                                                      kps, part, un2p, wnp, clear);
+      const int64_t n = T * E, threads = n + T + E;
+      router_reduce_kernel<<<dim3((unsigned)((threads + 255) / 256)), 256, 0, st>>>(part, S, n, E, bias, logits, T,
+                                                                                   un2p, wnp, un2, wn);
     }
   } else {
-    row_norm2_kernel<false><<<dim3((unsigned)((T + 3) / 4)), 256, 0, st>>>(u, T, d, un2);
-    row_norm2_kernel<false, true><<<dim3((unsigned)((E + 3) / 4)), 256, 0, st>>>(w_router, E, d, wn);
     dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16));
-    router_logits_f32_kernel<<<grid, 256, 0, st>>>((const float *)u, (const float *)w_router, bias, T, E, d, logits);
+    router_logits_f32_kernel<<<grid, 256, 0, st>>>((const float *)u, (const float *)w_router, bias, T, E, d, logits,
+                                                   un2, wn, clear);
   }
   return hipGetLastError();
 }
