@@ -1,4 +1,5 @@
-"""GPU parity of the router's wide tiles (64 tokens x 256 experts per work-group).
+"""GPU parity of the router's wide tiles (64 tokens x 256 experts per work-group)
+and of the two top-k kernels' division of labour.
 
 The bf16 router takes these tiles when they alone give at least 256
 work-groups, with at least 192 routed experts.  The cases below sit just past
@@ -10,11 +11,12 @@ bit, and the kept gates to the usual tolerance.
 """
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import workloads
-from fine_grained_routed_amd import MoELayer
-from tests.parity import GATE_TOL, gpu_inputs, log, oracle_args
+from fine_grained_routed_amd import PATH_PREFILL, MoELayer
+from tests.parity import GATE_TOL, check_case, gpu_inputs, log, oracle_args
 
 pytestmark = pytest.mark.gpu
 
@@ -49,3 +51,49 @@ def test_wide_router_tiles_match_the_oracle(lib, name, T, d, E, k, bias):
     gerr = float(np.max(np.abs(gw.cpu().numpy().astype(np.float64) - gw_o)))
     assert gerr <= GATE_TOL, gerr
     assert diag["flags"] == 0, diag
+
+
+# ------------------------------------------------------------- top-k kernels
+# Above 1024 tokens the top-k runs one wavefront per token (levels 1 and 2)
+# and lists the tokens that need exact keys for the cooperative kernel; up to
+# 1024 it runs the cooperative kernel (four wavefronts per token) for every
+# token.  These cases drive the list and the switch.
+
+def _tie_case(T, **kw):
+    # zero router: every logit is exactly 0, so every round of every token
+    # needs exact keys (the lower index wins)
+    wl = workloads.Workload("tie_big", T, 256, 64, 128, 1, 6, "bf16", None, "tie_big", "edge case")
+    inp = gpu_inputs(wl)
+    inp["w_router"].zero_()
+    layer = MoELayer({k: v for k, v in inp.items() if k != "u"}, wl.top_k, **kw)
+    return wl, inp, layer
+
+
+def test_large_batch_exact_ties_go_through_the_list(lib):
+    wl, inp, layer = _tie_case(1500)
+    r = check_case(layer, inp, wl, path=PATH_PREFILL, sample=256)
+    assert r["diag"]["tokens_exact"] == 1500
+    assert r["diag"]["exact_keys"] > 0
+
+
+def test_large_batch_group_limit_with_ties(lib):
+    wl, inp, layer = _tie_case(1200, n_group=16, topk_group=2)
+    check_case(layer, inp, wl, path=PATH_PREFILL, sample=256)
+
+
+def test_topk_kernels_agree_across_the_switch(lib):
+    # the same tokens routed by the cooperative kernel (a batch of 1024) and by
+    # the one-wavefront kernel (the same 1024 tokens plus one)
+    wl = workloads.Workload("switch", 1025, 512, 256, 64, 1, 8, "bf16", "zipf1.2", "switch", "top-k switch")
+    inp = gpu_inputs(wl, seed=3)
+    layer = MoELayer({k: v for k, v in inp.items() if k != "u"}, wl.top_k)
+    idx_a, gw_a = layer.router_topk(inp["u"][:1024].contiguous())
+    diag_a = layer.diagnostics()
+    idx_b, gw_b = layer.router_topk(inp["u"])
+    log(f"[router] switch: coop diagnostics {diag_a}, one-wave {layer.diagnostics()}")
+    assert torch.equal(idx_a, idx_b[:1024])
+    # refined logits may differ in their last bits (different fp64 sum orders)
+    assert float((gw_a - gw_b[:1024]).abs().max()) <= 1e-6
+    a = oracle_args(inp)
+    idx_o, _, _, _ = oracle.route(workloads.to_f64(inp["u"]), a["w_router"], wl.top_k, a["bias"])
+    assert np.array_equal(idx_b.cpu().numpy(), idx_o)
