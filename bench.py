@@ -105,6 +105,31 @@ def timed_steps(step, steps, warmup, hev, stages=STAGES, between=None, per_step=
     return wall_ms, sum(totals) / steps, stage
 
 
+def graph_ms_per_step(fn, steps, warmup):
+    """Wall time per call of fn() replayed from one captured HIP graph: the same
+    kernels as the eager calls, without the host's launch cost between them
+    (the way a serving loop would run small batches)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
 class _TimedWidening:
     """Expert stack view for the oracle that widens expert e's bf16/fp32 matrix to
     fp64 when the oracle asks for it and adds the time spent widening to a
@@ -259,6 +284,10 @@ def main():
     per_step = []
     wall_ms, ev_ms, stage = timed_steps(step, args.steps, args.warmup, hev, stages, between, per_step)
     per_step.sort()
+    graph_ms = None
+    if not between:
+        print("[bench] timing the same step replayed from a HIP graph", file=sys.stderr, flush=True)
+        graph_ms = graph_ms_per_step(lambda: step(None), args.steps, args.warmup)
 
     R = T * wl.top_k
     gu_flop = 4.0 * wl.d * (R * wl.d_ff + T * wl.d_ff_shared)
@@ -302,8 +331,11 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "grouped_gemm_bf16_kernel<gate_up>",
                      "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": gu_tflops / PEAK_BF16_TFLOPS,
+                     # the committed counters were taken on the two DeepSeek-V3 prefill workloads only
                      "traffic": measured_traffic("dense_gate_up_prefill" if dense else "gate_up_prefill",
-                                                 "ffn_prefill.hip") if not (args.block or cap or ng) else None,
+                                                 "ffn_prefill.hip")
+                     if wl.name in ("dsv3_prefill", "dsv3_dense_prefill") and not (args.block or cap or ng)
+                     else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         "layer_tflops": total_flop / (wall_ms * 1e-3) / 1e12,
         "layer_frac_of_peak": total_flop / (wall_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -313,6 +345,7 @@ def main():
         "event_ms_min": per_step[0],
         "flush_mb_between_steps": args.flush_mb,
         "down_tflops": dn_flop / (stage["down"] * 1e-3) / 1e12,
+        "graph": None if graph_ms is None else {"ms_per_step": graph_ms, "tokens_per_s": T / (graph_ms * 1e-3)},
     }
     if args.block:
         eb = 2 if wl.dtype == "bf16" else 4
@@ -341,8 +374,10 @@ def main():
         gu_bytes = eb * (touched * 2 * wl.d_ff * wl.d + 2 * wl.d_ff_shared * wl.d)
         dn_bytes = eb * (touched * wl.d * wl.d_ff + wl.d * wl.d_ff_shared)
         layer_bytes = gu_bytes + dn_bytes + eb * (wl.n_routed * wl.d + dec.T * wl.d) + 4 * dec.T * wl.d
+        d_graph = graph_ms_per_step(lambda: layer.forward(ud, path=PATH_DECODE), max(args.steps, 20), args.warmup)
         result["decode"] = {
             "workload": dec.name, "T": dec.T, "tokens_per_s": dec.T / (d_wall * 1e-3), "ms_per_step": d_wall,
+            "graph": {"ms_per_step": d_graph, "tokens_per_s": dec.T / (d_graph * 1e-3)},
             "touched_experts": touched, "stage_ms": d_stage,
             "layer_GBps": layer_bytes / (d_wall * 1e-3) / 1e9,
             "layer_frac_hbm": layer_bytes / (d_wall * 1e-3) / 1e9 / PEAK_HBM_GBS,

@@ -12,8 +12,10 @@ from tests.parity import gpu_inputs, log
 
 pytestmark = pytest.mark.gpu
 
+# skew512 at its full 8192 tokens takes the router's wide tiles and the two
+# top-k kernels (one wavefront per token, then the exact-key list)
 CASES = [("dsmoe16b", 200, PATH_PREFILL), ("dsv3_decode", None, PATH_DECODE), ("tiny_f32", None, PATH_AUTO),
-         ("dense_small", 300, PATH_AUTO)]
+         ("dense_small", 300, PATH_AUTO), ("skew512", None, PATH_PREFILL)]
 
 
 @pytest.mark.parametrize("name,T,path", CASES, ids=[f"{c[0]}-T{c[1]}-p{c[2]}" for c in CASES])
