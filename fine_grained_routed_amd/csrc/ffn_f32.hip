@@ -93,13 +93,28 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgsF a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) bcol[j] = GATEUP ? ((j >> 1) * 32 + tx * 2 + (j & 1)) : (tx * 4 + j);
   float acc[4][4] = {};
+  // the next k-tile's elements are loaded into registers while the current
+  // one is multiplied (the same additions in the same order)
+  float na[4], nb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    na[q] = ap[q][0];
+    nb[q] = bok[q] ? bp[q][0] : 0.f;
+  }
   for (int k0 = 0; k0 < K; k0 += F_BK) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      As[lr[q]][lc[q]] = ap[q][k0];
-      Bs[lr[q]][lc[q]] = bok[q] ? bp[q][k0] : 0.f;
+      As[lr[q]][lc[q]] = na[q];
+      Bs[lr[q]][lc[q]] = nb[q];
     }
     __syncthreads();
+    if (k0 + F_BK < K) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        na[q] = ap[q][k0 + F_BK];
+        nb[q] = bok[q] ? bp[q][k0 + F_BK] : 0.f;
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < F_BK; ++kk) {
       float av[4], bv[4];
