@@ -75,6 +75,7 @@ struct GemmArgs {
   int E, K, K_sh, N, N_sh, has_shared;
   int bnt;                   // single-m-tile experts' weights by non-temporal DMA
   int nt_r, nt_s;            // column tiles of a routed / the shared group
+  int mt_s;                  // m-tiles of the shared group (0 without one)
 };
 
 // element offset of 16-byte chunk c of LDS row r
@@ -321,60 +322,67 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(GemmArgs a) {
   // expert, its ragged tail included) run at the same time and share it in
   // L2, while neighbouring column tiles share the token rows.  Each XCD walks
   // a contiguous range of this order.
-  const int mt_r = a.tile_off[a.E];
-  const int mt_s = a.tile_off[a.E + 1] - mt_r;
-  const int64_t tiles_r = (int64_t)mt_r * a.nt_r;
-  const int64_t total = tiles_r + (int64_t)mt_s * a.nt_s;
-  constexpr int CH = GATEUP ? PF_CHUNK_GU : PF_CHUNK_DN;
-  const int64_t slot = blockIdx.x >> 3;
-  const int64_t tile = ((slot / CH) * 8 + (blockIdx.x & 7)) * CH + slot % CH;
+  // All tile indices are below 2^24 (the host bounds the grid), so the
+  // decoding below runs in 32-bit arithmetic.
+  const uint32_t tiles_r = (uint32_t)a.tile_off[a.E] * (uint32_t)a.nt_r;
+  const uint32_t total = tiles_r + (uint32_t)a.mt_s * (uint32_t)a.nt_s;
+  constexpr uint32_t CH = GATEUP ? PF_CHUNK_GU : PF_CHUNK_DN;
+  const uint32_t slot = blockIdx.x >> 3;
+  const uint32_t tile = ((slot / CH) * 8 + (blockIdx.x & 7)) * CH + slot % CH;
   if (tile >= total) return;
 
   bool shared;
   int g, nt, K, N, valid;
   int64_t rb;  // first row of this tile in the group's row space
-  int mt, mt_g, ntiles, gm;
-  int64_t q;   // index of the tile inside its group
+  int mt, mt_g, gm, rows, row0;
+  uint32_t q, ntiles;  // q: index of the tile inside its group
   if (tile < tiles_r) {
     shared = false;
-    const int key = (int)(tile / a.nt_r);  // expert g owns keys tile_off[g] .. tile_off[g+1]-1
-    int lo = 0, hi = a.E - 1;              // largest g with tile_off[g] <= key
+    const int key = (int)(tile / (uint32_t)a.nt_r);  // expert g owns keys tile_off[g] .. tile_off[g+1]-1
+    int lo = 0, hi = a.E - 1;                       // largest g with tile_off[g] <= key
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (a.tile_off[mid] <= key) lo = mid; else hi = mid - 1;
     }
     g = lo;
-    q = tile - (int64_t)a.nt_r * a.tile_off[g];
-    mt_g = a.tile_off[g + 1] - a.tile_off[g];
+    const int k0 = a.tile_off[g];
+    q = tile - (uint32_t)a.nt_r * (uint32_t)k0;
+    mt_g = a.tile_off[g + 1] - k0;
     ntiles = a.nt_r;
     gm = PF_GM;
     K = a.K;
     N = a.N;
+    row0 = a.offsets[g];
+    rows = a.offsets[g + 1] - row0;
   } else {
     shared = true;
     g = a.E;
     q = tile - tiles_r;
-    mt_g = mt_s;
+    mt_g = a.mt_s;
     ntiles = a.nt_s;
     gm = PF_GM_SH;
     K = a.K_sh;
     N = a.N_sh;
+    row0 = 0;
+    rows = (int)a.T;
   }
   {
-    const int64_t blk = q / ((int64_t)gm * ntiles);       // full blocks of gm m-tiles before
-    const int in_blk = (int)(q - blk * gm * ntiles);
-    const int bsize = min(gm, mt_g - (int)blk * gm);       // m-tiles in this block
-    nt = in_blk / bsize;
-    mt = (int)blk * gm + in_blk % bsize;
+    const uint32_t per = (uint32_t)gm * ntiles;       // tiles in a full block of gm m-tiles
+    const uint32_t blk = q / per;
+    const uint32_t in_blk = q - blk * per;
+    const uint32_t bsize = (uint32_t)min(gm, mt_g - (int)blk * gm);  // m-tiles in this block
+    const uint32_t n = in_blk / bsize;
+    nt = (int)n;
+    mt = (int)(blk * gm + (in_blk - n * bsize));
   }
   // the group's rows are cut into its mt_g tiles as evenly as possible (all
-  // of them at most 256 rows), so a group slightly over a multiple of 256 rows
-  // gets tiles of nearly equal size rather than a nearly empty last tile
+  // of them at most 256 rows; the first rows % mt_g tiles take one row more),
+  // so a group slightly over a multiple of 256 rows gets tiles of nearly
+  // equal size rather than a nearly empty last tile
   {
-    const int64_t rows = shared ? a.T : (int64_t)(a.offsets[g + 1] - a.offsets[g]);
-    const int64_t r0 = (int64_t)mt * rows / mt_g, r1 = (int64_t)(mt + 1) * rows / mt_g;
-    valid = (int)(r1 - r0);
-    rb = (shared ? 0 : (int64_t)a.offsets[g]) + r0;
+    const int base = rows / mt_g, rem = rows - base * mt_g;
+    valid = base + (mt < rem ? 1 : 0);
+    rb = (int64_t)row0 + (int64_t)mt * base + min(mt, rem);
   }
   const int wm = wv >> 1, wn = wv & 1;  // 2 x 2 wave layout
   // the tile's 32-row sub-tiles, split as evenly as possible between the two
@@ -586,6 +594,7 @@ hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u,
   g1.has_shared = hs;
   g1.nt_r = (f + PF_BN / 2 - 1) / (PF_BN / 2);
   g1.nt_s = hs ? (fs + PF_BN / 2 - 1) / (PF_BN / 2) : 1;
+  g1.mt_s = (int)mt_sh;
   // routed experts with a single m-tile read each gate/up weight line once, so
   // their tiles stream the weights non-temporally (DeepSeek-V3 gate/up 8%
   // faster at T = 512-1024, 5.5% at 2048, 1.7% at 4096); the down projection
@@ -617,6 +626,7 @@ hipError_t launch_ffn_prefill_bf16(const moe_dims &dm, int64_t T, const void *u,
   g2.has_shared = hs;
   g2.nt_r = (d + PF_BN - 1) / PF_BN;
   g2.nt_s = g2.nt_r;
+  g2.mt_s = (int)mt_sh;
   g2.bnt = 0;
   grouped_gemm_bf16_kernel<false><<<dim3((unsigned)grid2), 256, 0, st>>>(g2);
   return hipGetLastError();
