@@ -141,6 +141,9 @@ struct DiagWords {
 #define MOE_N_BM 5
 __host__ __device__ constexpr int moe_bm_of(int i) { return 16 << i; }  // 16 32 64 128 256
 
+// Largest top-k a layer may have (kernels hold a token's slots in registers).
+#define MOE_MAX_TOPK 16
+
 // Tokens per call (keeps the per-token dispatches under 2^32 work-items).
 #define MOE_MAX_TOKENS (1 << 22)
 

@@ -59,7 +59,7 @@ static moe_status check_dims(const moe_dims *dm, int64_t T) {
   if (dm->dtype != MOE_F32 && dm->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dm->dtype);
   if (dm->out_dtype != MOE_F32 && dm->out_dtype != MOE_BF16)
     return fail(MOE_ERR_UNSUPPORTED, "unknown out_dtype %d", dm->out_dtype);
-  if (dm->top_k > 16) return fail(MOE_ERR_UNSUPPORTED, "top_k > 16");
+  if (dm->top_k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "top_k > 16");
   if (dm->n_routed > 1024) return fail(MOE_ERR_UNSUPPORTED, "n_routed > 1024");
   if (dm->d_model < 64 || dm->d_model > 32768 || dm->d_model % 64)
     return fail(MOE_ERR_UNSUPPORTED, "d_model must be a multiple of 64 in [64, 32768]");

@@ -22,24 +22,57 @@
 
 #define PERM_WORDS (MOE_PERM_BLOCK / 64)
 
-__device__ __forceinline__ void build_bitmap(unsigned long long *bm, const int32_t *__restrict__ idx, int64_t T,
-                                             int E, int k, int64_t blk, DiagWords *diag) {
+// The k expert indices of token t, all loads issued before the first use
+// (slots j >= k hold -1, never read).
+__device__ __forceinline__ void load_slots(const int32_t *__restrict__ idx, int64_t t, int k,
+                                           int (&ev)[MOE_MAX_TOPK]) {
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) ev[j] = j < k ? idx[t * k + j] : -1;
+}
+
+// Set bits of an expert's block bitmap below bit i: the tokens of the block
+// before token i that chose the expert.
+__device__ __forceinline__ int bits_below(const unsigned long long *row, int i) {
+  const int w = i >> 6;
+  int n = 0;
+#pragma unroll
+  for (int q = 0; q < PERM_WORDS; ++q)
+    if (q < w) n += __popcll(row[q]);
+  return n + __popcll((i & 63) ? (row[w] & ((1ull << (i & 63)) - 1ull)) : 0ull);
+}
+
+// Sets token i's bit in the bitmap of each expert among its k slots (ev);
+// an index out of range or a repeated expert is flagged in diag (if given).
+__device__ __forceinline__ void mark_slots(unsigned long long *bm, const int (&ev)[MOE_MAX_TOPK], int i, int E, int k,
+                                           DiagWords *diag) {
+  const unsigned long long bit = 1ull << (i & 63);
+  // every atomic is issued before the first result is looked at (an out of
+  // range index ORs 0 into expert 0's word, a no-op)
+  unsigned long long old[MOE_MAX_TOPK];
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    const int e = ev[j];
+    const bool ok = e >= 0 && e < E;
+    old[j] = j < k ? atomicOr(&bm[(ok ? e : 0) * PERM_WORDS + (i >> 6)], ok ? bit : 0ull) : 0ull;
+    bad |= j < k && !ok;
+  }
+  unsigned long long seen = 0;  // token i's bit was already set in one of its experts' bitmaps
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    const int e = ev[j];
+    if (j < k && e >= 0 && e < E) seen |= old[j] & bit;
+  }
+  if (diag && (seen || bad)) atomicOr(&diag->flags, (seen ? MOE_DIAG_DUPLICATE : 0u) | (bad ? MOE_DIAG_BAD_INDEX : 0u));
+}
+
+// Bit i of word (i / 64) of expert e's bitmap: token i of the block (thread
+// i, whose slots are ev when it has a token) chose e.
+__device__ __forceinline__ void build_bitmap(unsigned long long *bm, const int (&ev)[MOE_MAX_TOPK], bool has_token,
+                                             int E, int k, DiagWords *diag) {
   for (int i = threadIdx.x; i < E * PERM_WORDS; i += blockDim.x) bm[i] = 0ull;
   __syncthreads();
-  const int i = threadIdx.x;
-  const int64_t t = blk * MOE_PERM_BLOCK + i;
-  if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j];
-      if (e < 0 || e >= E) {
-        if (diag) atomicOr(&diag->flags, MOE_DIAG_BAD_INDEX);
-        continue;
-      }
-      const unsigned long long bit = 1ull << (i & 63);
-      const unsigned long long old = atomicOr(&bm[e * PERM_WORDS + (i >> 6)], bit);
-      if ((old & bit) && diag) atomicOr(&diag->flags, MOE_DIAG_DUPLICATE);
-    }
-  }
+  if (has_token) mark_slots(bm, ev, threadIdx.x, E, k, diag);
   __syncthreads();
 }
 
@@ -47,7 +80,10 @@ __global__ __launch_bounds__(MOE_PERM_BLOCK) void perm_hist_kernel(const int32_t
                                                                    int k, int32_t *__restrict__ blk_hist,
                                                                    DiagWords *diag) {
   extern __shared__ unsigned long long bm[];
-  build_bitmap(bm, idx, T, E, k, blockIdx.x, diag);
+  const int64_t t = (int64_t)blockIdx.x * MOE_PERM_BLOCK + threadIdx.x;
+  int ev[MOE_MAX_TOPK];
+  load_slots(idx, t, t < T ? k : 0, ev);
+  build_bitmap(bm, ev, t < T, E, k, diag);
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int c = 0;
 #pragma unroll
@@ -108,10 +144,17 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ b
   const int e = threadIdx.x;
   int tot = 0;
   if (e < E) {
-    for (int64_t b = 0; b < nblk; ++b) {
-      const int c = blk_hist[b * E + e];
-      blk_hist[b * E + e] = tot;  // the expert's pairs in earlier blocks: the block's first rank
-      tot += c;
+    // 16 blocks' counts loaded at a time, then replaced by the expert's pairs
+    // in earlier blocks (the block's first rank)
+    for (int64_t b0 = 0; b0 < nblk; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) c[q] = b0 + q < nblk ? blk_hist[(b0 + q) * E + e] : 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (b0 + q < nblk) blk_hist[(b0 + q) * E + e] = tot;
+        tot += c[q];
+      }
     }
   }
   const int seats = (cap > 0 && tot > cap) ? cap : tot;
@@ -131,32 +174,26 @@ __global__ __launch_bounds__(MOE_PERM_BLOCK) void perm_scatter_kernel(const int3
                                                                       int32_t *__restrict__ row_token,
                                                                       int32_t *__restrict__ token_row) {
   extern __shared__ unsigned long long bm[];
-  build_bitmap(bm, idx, T, E, k, blockIdx.x, nullptr);
   const int i = threadIdx.x;
   const int64_t t = (int64_t)blockIdx.x * MOE_PERM_BLOCK + i;
+  int ev[MOE_MAX_TOPK];
+  load_slots(idx, t, t < T ? k : 0, ev);
+  build_bitmap(bm, ev, t < T, E, k, nullptr);
   if (t >= T) return;
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[t * k + j];
-    if (e < 0 || e >= E) {
-      token_row[t * k + j] = -1;
-      continue;
-    }
-    const unsigned long long *row = bm + e * PERM_WORDS;
-    int rank = 0;
-    const int w = i >> 6;
 #pragma unroll
-    for (int q = 0; q < PERM_WORDS; ++q)
-      if (q < w) rank += __popcll(row[q]);
-    const unsigned long long below = (i & 63) ? (row[w] & ((1ull << (i & 63)) - 1ull)) : 0ull;
-    rank += __popcll(below);
-    rank += blk_base[(int64_t)blockIdx.x * E + e];  // rank among all of the expert's pairs
-    if (cap > 0 && rank >= cap) {
-      token_row[t * k + j] = -1;  // no seat left
-      continue;
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j < k) {
+      const int e = ev[j];
+      int r = -1;  // dropped: invalid index or no seat left
+      if (e >= 0 && e < E) {
+        // rank among all of the expert's pairs: the block's first rank plus
+        // the bits below this token's
+        int rank = blk_base[(int64_t)blockIdx.x * E + e] + bits_below(bm + e * PERM_WORDS, i);
+        if (!(cap > 0 && rank >= cap)) r = offsets[e] + rank;
+      }
+      token_row[t * k + j] = r;
+      if (r >= 0) row_token[r] = (int32_t)t;
     }
-    const int r = offsets[e] + rank;
-    token_row[t * k + j] = r;
-    row_token[r] = (int32_t)t;
   }
 }
 
@@ -175,19 +212,10 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
   __shared__ int sh[1024];
   const int tid = threadIdx.x;
   for (int i = tid; i < E * PERM_WORDS; i += 1024) bm[i] = 0ull;
+  int ev[MOE_MAX_TOPK];
+  load_slots(idx, tid, tid < T ? k : 0, ev);
   __syncthreads();
-  if (tid < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(int64_t)tid * k + j];
-      if (e < 0 || e >= E) {
-        atomicOr(&diag->flags, MOE_DIAG_BAD_INDEX);
-        continue;
-      }
-      const unsigned long long bit = 1ull << (tid & 63);
-      const unsigned long long old = atomicOr(&bm[e * PERM_WORDS + (tid >> 6)], bit);
-      if (old & bit) atomicOr(&diag->flags, MOE_DIAG_DUPLICATE);
-    }
-  }
+  if (tid < T) mark_slots(bm, ev, tid, E, k, diag);
   __syncthreads();
   int tot = 0;
   if (tid < E) {
@@ -222,25 +250,18 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
   __syncthreads();
   if (tid < T) {
     const int w = tid >> 6;
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[(int64_t)tid * k + j];
-      if (e < 0 || e >= E) {
-        token_row[(int64_t)tid * k + j] = -1;
-        continue;
-      }
-      const unsigned long long *row = bm + e * PERM_WORDS;
-      int rank = 0;
 #pragma unroll
-      for (int q = 0; q < PERM_WORDS; ++q)
-        if (q < w) rank += __popcll(row[q]);
-      rank += __popcll((tid & 63) ? (row[w] & ((1ull << (tid & 63)) - 1ull)) : 0ull);
-      if (cap > 0 && rank >= cap) {
-        token_row[(int64_t)tid * k + j] = -1;  // no seat left
-        continue;
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k) {
+        const int e = ev[j];
+        int r = -1;  // dropped: invalid index or no seat left
+        if (e >= 0 && e < E) {
+          const int rank = bits_below(bm + e * PERM_WORDS, tid);
+          if (!(cap > 0 && rank >= cap)) r = start[e] + rank;
+        }
+        token_row[(int64_t)tid * k + j] = r;
+        if (r >= 0) row_token[r] = tid;
       }
-      const int r = start[e] + rank;
-      token_row[(int64_t)tid * k + j] = r;
-      row_token[r] = tid;
     }
   }
 }

@@ -126,11 +126,13 @@ def test_paths_agree(lib):
     assert rel_err(q, p) <= 1e-2
 
 
-def test_permute_flags_bad_indices(lib):
-    wl = _wl(300, 128, 8, 64, 0, 2, name="bad_idx")
+@pytest.mark.parametrize("T", [300, 200], ids=["blocks", "one_launch"])
+def test_permute_flags_bad_indices(lib, T):
+    # 300 tokens: the three-launch permutation; 200: the one-launch form
+    wl = _wl(T, 128, 8, 64, 0, 2, name="bad_idx")
     inp = gpu_inputs(wl)
     layer = _layer(inp, wl)
-    idx = torch.tensor([[0, 1]] * 300, dtype=torch.int32, device="cuda")
+    idx = torch.tensor([[0, 1]] * T, dtype=torch.int32, device="cuda")
     idx[7, 1] = 8        # out of range
     idx[9] = torch.tensor([3, 3], dtype=torch.int32)  # duplicate
     counts, offsets, row_token, token_row = layer.permute(idx)
