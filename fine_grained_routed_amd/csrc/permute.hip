@@ -92,38 +92,55 @@ __global__ __launch_bounds__(MOE_PERM_BLOCK) void perm_hist_kernel(const int32_t
   }
 }
 
+// Inclusive scan over the 64 lanes of a wave with DPP: shifts by 1, 2, 4 and
+// 8 inside each row of 16 lanes (lanes shifted in from outside the row read
+// 0), then row 0's total added to row 1 and row 2's to row 3 (the broadcast
+// of lane 15 of each row), then the total of rows 0-1 added to rows 2 and 3
+// (the broadcast of lane 31).  Every lane of the wave must be active.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Exclusive scans of the N values v[n] over the work-group (blockDim.x a
 // multiple of 64, at most 1024): excl[n] is this thread's prefix, total[n]
-// the sum.  Each wave scans in registers (shuffles), the wave totals meet in
-// LDS (sh: 16 N ints) behind one barrier, and a second barrier frees sh.
-// Integer sums: the result does not depend on the order.
+// the sum.  Each wave scans in registers (DPP), the wave totals meet in
+// LDS (sh: 16 N ints, value-major) behind one barrier, and a second barrier
+// frees sh.  Integer sums: the result does not depend on the order.
 template <int N>
 __device__ __forceinline__ void block_scan_n(const int (&v)[N], int (&excl)[N], int (&total)[N], int *sh) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
   int incl[N];
 #pragma unroll
-  for (int n = 0; n < N; ++n) incl[n] = v[n];
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1)
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-      const int y = __shfl_up(incl[n], o, 64);
-      if (lane >= o) incl[n] += y;
-    }
+  for (int n = 0; n < N; ++n) incl[n] = wave_incl_scan(v[n]);
   if (lane == 63)
 #pragma unroll
-    for (int n = 0; n < N; ++n) sh[wv * N + n] = incl[n];
+    for (int n = 0; n < N; ++n) sh[n * 16 + wv] = incl[n];
   __syncthreads();
+  // every wave then scans the wave totals itself: lane l < 16 holds wave l's
+  // (0 past the last wave), an inclusive scan over the 16 lanes of DPP row 0
+  // (shifts 1, 2, 4, 8), and the wave reads its prefix and the total from
+  // lanes wv - 1 and 15
+  const int l16 = lane & 15;
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);
+  int x[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) x[n] = sh[n * 16 + l16];
 #pragma unroll
   for (int n = 0; n < N; ++n) {
-    int pre = 0, tot = 0;
-    for (int w2 = 0; w2 < nw; ++w2) {
-      const int x = sh[w2 * N + n];
-      pre += w2 < wv ? x : 0;
-      tot += x;
-    }
+    int sc = l16 < nw ? x[n] : 0;
+    sc += __builtin_amdgcn_update_dpp(0, sc, 0x111, 0xf, 0xf, true);  // row_shr:1
+    sc += __builtin_amdgcn_update_dpp(0, sc, 0x112, 0xf, 0xf, true);  // row_shr:2
+    sc += __builtin_amdgcn_update_dpp(0, sc, 0x114, 0xf, 0xf, true);  // row_shr:4
+    sc += __builtin_amdgcn_update_dpp(0, sc, 0x118, 0xf, 0xf, true);  // row_shr:8
+    const int pre = wvs > 0 ? __builtin_amdgcn_readlane(sc, wvs - 1) : 0;
     excl[n] = pre + incl[n] - v[n];
-    total[n] = tot;
+    total[n] = __builtin_amdgcn_readlane(sc, 15);
   }
   __syncthreads();
 }
@@ -140,7 +157,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *sh, int *total) 
 // cap: seats per expert, 0 = no limit
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ blk_hist, int64_t nblk, int E, int cap,
                                                          int32_t *__restrict__ counts, int32_t *__restrict__ offsets) {
-  __shared__ int sh[1024];
+  __shared__ __attribute__((aligned(16))) int sh[16];
   const int e = threadIdx.x;
   int tot = 0;
   if (e < E) {
@@ -209,7 +226,7 @@ __global__ __launch_bounds__(1024) void perm_small_kernel(const int32_t *__restr
                                                           int32_t *__restrict__ tile_off, DiagWords *diag) {
   extern __shared__ unsigned long long bm[];  // [E][PERM_WORDS] bitmap, then int[E] group starts
   int *start = (int *)(bm + E * PERM_WORDS);
-  __shared__ int sh[1024];
+  __shared__ __attribute__((aligned(16))) int sh[16 * (1 + MOE_N_BM)];
   const int tid = threadIdx.x;
   for (int i = tid; i < E * PERM_WORDS; i += 1024) bm[i] = 0ull;
   int ev[MOE_MAX_TOPK];
@@ -299,7 +316,7 @@ hipError_t launch_permute(const moe_dims &dm, int64_t T, const int32_t *topk_idx
 // g <= E, and tile_off[b][E+1] adds the shared group's ceil(T / BM_b) m-tiles.
 __global__ __launch_bounds__(1024) void tile_offsets_kernel(const int32_t *__restrict__ counts, int E, int64_t T,
                                                             int has_shared, int32_t *__restrict__ tile_off) {
-  __shared__ int sh[1024];
+  __shared__ __attribute__((aligned(16))) int sh[16 * MOE_N_BM];
   const int e = threadIdx.x;
   const int c = e < E ? counts[e] : 0;
   int v[MOE_N_BM], ex[MOE_N_BM], all[MOE_N_BM];
