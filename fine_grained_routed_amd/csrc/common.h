@@ -87,6 +87,48 @@ __device__ __forceinline__ void publish() {
 }
 
 // ------------------------------------------------------------ wave reductions
+// Wave-wide fp64 max and sum, uniform: four DPP steps (lane i meets lanes
+// i ^ 1, i ^ 2, then its mirror in 8 and in 16) leave every row of 16 lanes
+// holding its row's result; two row broadcasts then fold row 0 into row 1,
+// row 2 into row 3 and row 1 into row 3, and lane 63's value is the result.
+// The order of the additions is fixed, so the sum is reproducible.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double old, double v) {
+  const long long o = __double_as_longlong(old), b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp((int)o, (int)b, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(o >> 32), (int)(b >> 32), CTRL, ROWS, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, l), hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+#define DPP_XOR1 0xB1       // quad_perm [1, 0, 3, 2]
+#define DPP_XOR2 0x4E       // quad_perm [2, 3, 0, 1]
+#define DPP_HALF_MIRROR 0x141
+#define DPP_MIRROR 0x140
+#define DPP_BCAST15 0x142   // lane 15 of each row into the next row
+#define DPP_BCAST31 0x143   // lane 31 into rows 2 and 3
+__device__ __forceinline__ double dpp_wave_max_f64(double v) {
+  v = fmax(v, dpp_f64<DPP_XOR1, 0xf>(v, v));
+  v = fmax(v, dpp_f64<DPP_XOR2, 0xf>(v, v));
+  v = fmax(v, dpp_f64<DPP_HALF_MIRROR, 0xf>(v, v));
+  v = fmax(v, dpp_f64<DPP_MIRROR, 0xf>(v, v));
+  v = fmax(v, dpp_f64<DPP_BCAST15, 0xa>(v, v));  // rows outside the mask keep v
+  v = fmax(v, dpp_f64<DPP_BCAST31, 0xc>(v, v));
+  return readlane_f64(v, 63);
+}
+__device__ __forceinline__ double dpp_wave_sum_f64(double v) {
+  v += dpp_f64<DPP_XOR1, 0xf>(0.0, v);
+  v += dpp_f64<DPP_XOR2, 0xf>(0.0, v);
+  v += dpp_f64<DPP_HALF_MIRROR, 0xf>(0.0, v);
+  v += dpp_f64<DPP_MIRROR, 0xf>(0.0, v);
+  v += dpp_f64<DPP_BCAST15, 0xa>(0.0, v);  // rows outside the mask add 0
+  v += dpp_f64<DPP_BCAST31, 0xc>(0.0, v);
+  return readlane_f64(v, 63);
+}
+
 __device__ __forceinline__ double wave_max_f64(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));

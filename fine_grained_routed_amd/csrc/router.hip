@@ -468,33 +468,46 @@ __global__ __launch_bounds__(256) void router_logits_f32_kernel(const float *__r
   const bool unorm = blockIdx.y == 0, cnorm = blockIdx.x == 0;
   double usq[4] = {0.0, 0.0, 0.0, 0.0}, csq[4] = {0.0, 0.0, 0.0, 0.0};
   double acc = 0.0;
-  for (int k0 = 0; k0 < d; k0 += 64) {
+  // the next k-tile's elements are loaded while the current one is summed
+  // (the same additions in the same order)
+  float na[4], nb[4];
+  auto load = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = wv + 4 * i;
       const int64_t tr = (int64_t)blockIdx.x * 16 + r;
       const int er = blockIdx.y * 16 + r;
-      const float av = tr < T ? u[tr * d + k0 + lane] : 0.f;
-      const float bv = er < E ? w[(int64_t)er * d + k0 + lane] : 0.f;
-      As[r][lane] = av;
-      Bs[r][lane] = bv;
-      if (unorm) usq[i] = fma((double)av, (double)av, usq[i]);
-      if (cnorm) csq[i] = fma((double)bv, (double)bv, csq[i]);
+      na[i] = tr < T ? u[tr * d + k0 + lane] : 0.f;
+      nb[i] = er < E ? w[(int64_t)er * d + k0 + lane] : 0.f;
+    }
+  };
+  load(0);
+  for (int k0 = 0; k0 < d; k0 += 64) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wv + 4 * i;
+      As[r][lane] = na[i];
+      Bs[r][lane] = nb[i];
+      if (unorm) usq[i] = fma((double)na[i], (double)na[i], usq[i]);
+      if (cnorm) csq[i] = fma((double)nb[i], (double)nb[i], csq[i]);
     }
     __syncthreads();
+    if (k0 + 64 < d) load(k0 + 64);
 #pragma unroll 8
     for (int kk = 0; kk < 64; ++kk) acc += (double)As[ty][kk] * (double)Bs[tx][kk];
     __syncthreads();
   }
   if (t < T && e < E) logits[t * E + e] = acc + (bias ? (double)bias[e] : 0.0);
+  if (unorm || cnorm) {  // only the first row and column of work-groups hold norms
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wv + 4 * i;
-    const double su = wave_sum_f64(usq[i]), sc = wave_sum_f64(csq[i]);
-    const int64_t tr = (int64_t)blockIdx.x * 16 + r;
-    const int er = blockIdx.y * 16 + r;
-    if (lane == 0 && unorm && tr < T) un2[tr] = su;
-    if (lane == 0 && cnorm && er < E) wn[er] = sqrt(sc);
+    for (int i = 0; i < 4; ++i) {
+      const int r = wv + 4 * i;
+      const double su = dpp_wave_sum_f64(usq[i]), sc = dpp_wave_sum_f64(csq[i]);
+      const int64_t tr = (int64_t)blockIdx.x * 16 + r;
+      const int er = blockIdx.y * 16 + r;
+      if (lane == 0 && unorm && tr < T) un2[tr] = su;
+      if (lane == 0 && cnorm && er < E) wn[er] = sqrt(sc);
+    }
   }
 }
 
