@@ -16,7 +16,12 @@
 // Y rows, Y_sh and the fp32 output are each touched once: non-temporal
 // accesses keep them from displacing other lines (measured 0.885 ms against
 // 0.963 ms at DeepSeek-V3 prefill).  One work-group of 512 threads per token
-// (0.86 ms against 0.88 with 256).
+// (0.86 ms against 0.88 with 256).  Each thread owns CB_NC float4 columns
+// 2048 apart and issues the loads of all of them (every slot and the shared
+// row) before its first addition, so a token's row is fetched in one round
+// trip instead of one per 2048 columns: 0.78 ms against 0.86 at DeepSeek-V3
+// prefill (6.0 TB/s), with 448, 384 and 1024 threads no better.  Top-k above
+// 9 keeps two chunks in flight, which fits the registers without spilling.
 __device__ __forceinline__ float4 load_once(const float *p) {
   const f32x4_t v = __builtin_nontemporal_load((const f32x4_t *)p);
   return make_float4(v[0], v[1], v[2], v[3]);
@@ -44,46 +49,58 @@ __global__ __launch_bounds__(512) void combine_kernel(const float *__restrict__ 
   }
   __syncthreads();
   const int64_t R = T * k;
-  for (int c = threadIdx.x * 4; c < d; c += 512 * 4) {
-    // every row of the token is loaded before the first addition, so the k
-    // loads are in flight together; the additions then run in slot order
-    float4 y[KM > 0 ? KM : 1];
+  constexpr int NC = (KM + 1) * 4 <= 40 ? 4 : 2;  // float4 chunks per thread per pass
+  for (int c0 = threadIdx.x * 4; c0 < d; c0 += 512 * 4 * NC) {
+    float4 y[NC][KM > 0 ? KM : 1];
+    float4 acc[NC];
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      const int64_t r = rows[j];        // -1 past the token's k slots or for a dropped pair
-      const bool ok = r >= 0 && r < R;  // an invalid row contributes nothing
-      const float4 v = load_once(y_rows + (ok ? r : 0) * d + c);
-      y[j] = make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
-    }
-    float4 acc = y_sh ? load_once(y_sh + t * d + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int cc = 0; cc < NC; ++cc) {
+      const int c = c0 + cc * 2048;
+      if (c < d) {
 #pragma unroll
-    for (int j = 0; j < KM; ++j) {
-      if (j < k) {
-        const float g = gw[j];
-        acc.x = fmaf(g, y[j].x, acc.x);
-        acc.y = fmaf(g, y[j].y, acc.y);
-        acc.z = fmaf(g, y[j].z, acc.z);
-        acc.w = fmaf(g, y[j].w, acc.w);
+        for (int j = 0; j < KM; ++j) {
+          const int64_t r = rows[j];        // -1 past the token's k slots or for a dropped pair
+          const bool ok = r >= 0 && r < R;  // an invalid row contributes nothing
+          const float4 v = load_once(y_rows + (ok ? r : 0) * d + c);
+          y[cc][j] = make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
+        }
+        acc[cc] = y_sh ? load_once(y_sh + t * d + c) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
-    if (RES == 1) {
-      const float4 x = *(const float4 *)((const float *)resid + t * d + c);
-      acc = make_float4(x.x + acc.x, x.y + acc.y, x.z + acc.z, x.w + acc.w);
-    } else if (RES == 2) {
-      const uint2 xb = *(const uint2 *)((const uint16_t *)resid + t * d + c);
-      acc.x = bf16_to_f32((uint16_t)xb.x) + acc.x;
-      acc.y = bf16_to_f32((uint16_t)(xb.x >> 16)) + acc.y;
-      acc.z = bf16_to_f32((uint16_t)xb.y) + acc.z;
-      acc.w = bf16_to_f32((uint16_t)(xb.y >> 16)) + acc.w;
-    }
-    if (OUT_BF16) {
-      uint16_t *o = (uint16_t *)out + t * d + c;
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
-      pk.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
-      *(uint2 *)o = pk;
-    } else {
-      store_once(acc, (float *)out + t * d + c);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const int c = c0 + cc * 2048;
+      if (c >= d) continue;
+      float4 a = acc[cc];
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (j < k) {
+          const float g = gw[j];
+          a.x = fmaf(g, y[cc][j].x, a.x);
+          a.y = fmaf(g, y[cc][j].y, a.y);
+          a.z = fmaf(g, y[cc][j].z, a.z);
+          a.w = fmaf(g, y[cc][j].w, a.w);
+        }
+      }
+      if (RES == 1) {
+        const float4 x = *(const float4 *)((const float *)resid + t * d + c);
+        a = make_float4(x.x + a.x, x.y + a.y, x.z + a.z, x.w + a.w);
+      } else if (RES == 2) {
+        const uint2 xb = *(const uint2 *)((const uint16_t *)resid + t * d + c);
+        a.x = bf16_to_f32((uint16_t)xb.x) + a.x;
+        a.y = bf16_to_f32((uint16_t)(xb.x >> 16)) + a.y;
+        a.z = bf16_to_f32((uint16_t)xb.y) + a.z;
+        a.w = bf16_to_f32((uint16_t)(xb.y >> 16)) + a.w;
+      }
+      if (OUT_BF16) {
+        uint16_t *o = (uint16_t *)out + t * d + c;
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
+        pk.y = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
+        *(uint2 *)o = pk;
+      } else {
+        store_once(a, (float *)out + t * d + c);
+      }
     }
   }
 }
