@@ -22,6 +22,9 @@
 // trip instead of one per 2048 columns: 0.78 ms against 0.86 at DeepSeek-V3
 // prefill (6.0 TB/s), with 448, 384 and 1024 threads no better.  Top-k above
 // 9 keeps two chunks in flight, which fits the registers without spilling.
+// Rows of at most 2048 columns have a single chunk: they take CB_NC = 1, since
+// registers held for absent chunks only cut occupancy (at d = 2048 the
+// four-chunk kernel took 0.12 against 0.094 ms, at d = 128 three times as long).
 __device__ __forceinline__ float4 load_once(const float *p) {
   const f32x4_t v = __builtin_nontemporal_load((const f32x4_t *)p);
   return make_float4(v[0], v[1], v[2], v[3]);
@@ -33,7 +36,8 @@ __device__ __forceinline__ void store_once(float4 a, float *p) {
 
 // KM: top_k rounded up to 0, 1, 2, 4, 8 or 16 (slots j >= k are predicated off;
 // 0 = dense layer, shared term only).  RES: 0 no residual, 1 fp32, 2 bf16 x.
-template <bool OUT_BF16, int KM, int RES>
+// WIDE: rows of more than 2048 columns (several chunks per thread).
+template <bool OUT_BF16, int KM, int RES, bool WIDE>
 __global__ __launch_bounds__(512) void combine_kernel(const float *__restrict__ y_rows, const float *__restrict__ y_sh,
                                                       const float *__restrict__ topk_w,
                                                       const int32_t *__restrict__ token_row,
@@ -49,7 +53,7 @@ __global__ __launch_bounds__(512) void combine_kernel(const float *__restrict__ 
   }
   __syncthreads();
   const int64_t R = T * k;
-  constexpr int NC = (KM + 1) * 4 <= 40 ? 4 : 2;  // float4 chunks per thread per pass
+  constexpr int NC = !WIDE ? 1 : (KM + 1) * 4 <= 40 ? 4 : 2;  // float4 chunks per thread per pass
   for (int c0 = threadIdx.x * 4; c0 < d; c0 += 512 * 4 * NC) {
     float4 y[NC][KM > 0 ? KM : 1];
     float4 acc[NC];
@@ -114,8 +118,12 @@ struct CombineCall {
 
 template <bool OUT_BF16, int KM, int RES>
 static void launch_combine_k(const moe_dims &dm, int64_t T, const CombineCall &c, hipStream_t st) {
-  combine_kernel<OUT_BF16, KM, RES><<<dim3((unsigned)T), 512, 0, st>>>(c.y_rows, c.y_sh, c.topk_w, c.token_row,
-                                                                       c.resid, T, dm.d_model, dm.top_k, c.out);
+  if (dm.d_model > 2048)
+    combine_kernel<OUT_BF16, KM, RES, true><<<dim3((unsigned)T), 512, 0, st>>>(c.y_rows, c.y_sh, c.topk_w, c.token_row,
+                                                                               c.resid, T, dm.d_model, dm.top_k, c.out);
+  else
+    combine_kernel<OUT_BF16, KM, RES, false><<<dim3((unsigned)T), 512, 0, st>>>(
+        c.y_rows, c.y_sh, c.topk_w, c.token_row, c.resid, T, dm.d_model, dm.top_k, c.out);
 }
 
 template <bool OUT_BF16, int RES>
