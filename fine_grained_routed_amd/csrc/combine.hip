@@ -57,6 +57,8 @@ __global__ __launch_bounds__(512) void combine_kernel(const float *__restrict__ 
   for (int c0 = threadIdx.x * 4; c0 < d; c0 += 512 * 4 * NC) {
     float4 y[NC][KM > 0 ? KM : 1];
     float4 acc[NC];
+    float4 xf[RES == 1 ? NC : 1];  // the residual row's chunks, loaded with the rest
+    uint2 xb[RES == 2 ? NC : 1];
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       const int c = c0 + cc * 2048;
@@ -69,6 +71,8 @@ __global__ __launch_bounds__(512) void combine_kernel(const float *__restrict__ 
           y[cc][j] = make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
         }
         acc[cc] = y_sh ? load_once(y_sh + t * d + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (RES == 1) xf[cc] = *(const float4 *)((const float *)resid + t * d + c);
+        if (RES == 2) xb[cc] = *(const uint2 *)((const uint16_t *)resid + t * d + c);
       }
     }
 #pragma unroll
@@ -87,14 +91,14 @@ __global__ __launch_bounds__(512) void combine_kernel(const float *__restrict__ 
         }
       }
       if (RES == 1) {
-        const float4 x = *(const float4 *)((const float *)resid + t * d + c);
+        const float4 x = xf[cc];
         a = make_float4(x.x + a.x, x.y + a.y, x.z + a.z, x.w + a.w);
       } else if (RES == 2) {
-        const uint2 xb = *(const uint2 *)((const uint16_t *)resid + t * d + c);
-        a.x = bf16_to_f32((uint16_t)xb.x) + a.x;
-        a.y = bf16_to_f32((uint16_t)(xb.x >> 16)) + a.y;
-        a.z = bf16_to_f32((uint16_t)xb.y) + a.z;
-        a.w = bf16_to_f32((uint16_t)(xb.y >> 16)) + a.w;
+        const uint2 x = xb[cc];
+        a.x = bf16_to_f32((uint16_t)x.x) + a.x;
+        a.y = bf16_to_f32((uint16_t)(x.x >> 16)) + a.y;
+        a.z = bf16_to_f32((uint16_t)x.y) + a.z;
+        a.w = bf16_to_f32((uint16_t)(x.y >> 16)) + a.w;
       }
       if (OUT_BF16) {
         uint16_t *o = (uint16_t *)out + t * d + c;
