@@ -16,13 +16,13 @@
 // Y rows, Y_sh and the fp32 output are each touched once: non-temporal
 // accesses keep them from displacing other lines (measured 0.885 ms against
 // 0.963 ms at DeepSeek-V3 prefill).  One work-group of 512 threads per token
-// (0.86 ms against 0.88 with 256).  Each thread owns CB_NC float4 columns
+// (0.86 ms against 0.88 with 256).  Each thread owns NC float4 columns
 // 2048 apart and issues the loads of all of them (every slot and the shared
 // row) before its first addition, so a token's row is fetched in one round
 // trip instead of one per 2048 columns: 0.78 ms against 0.86 at DeepSeek-V3
 // prefill (6.0 TB/s), with 448, 384 and 1024 threads no better.  Top-k above
 // 9 keeps two chunks in flight, which fits the registers without spilling.
-// Rows of at most 2048 columns have a single chunk: they take CB_NC = 1, since
+// Rows of at most 2048 columns have a single chunk: they take NC = 1, since
 // registers held for absent chunks only cut occupancy (at d = 2048 the
 // four-chunk kernel took 0.12 against 0.094 ms, at d = 128 three times as long).
 __device__ __forceinline__ float4 load_once(const float *p) {
