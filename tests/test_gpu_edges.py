@@ -161,3 +161,12 @@ def test_interface_limits(lib, path, T, d, E, f, k):
     wl = _wl(T, d, E, f, 1, k, name=f"limits_{d}_{E}")
     inp = gpu_inputs(wl, seed=9)
     check_case(_layer(inp, wl), inp, wl, path=path)
+
+
+@pytest.mark.parametrize("path", [PATH_PREFILL, PATH_DECODE])
+def test_wide_rows_with_large_top_k(lib, path):
+    # rows wider than 2048 columns with top-k above 9: the combine keeps two
+    # 2048-column chunks per thread in flight, the second one partly past d
+    wl = _wl(200, 2560, 32, 128, 1, 12, name="wide_k12")
+    inp = gpu_inputs(wl, seed=5)
+    check_case(_layer(inp, wl), inp, wl, path=path)
