@@ -1,17 +1,22 @@
 // Grouped expert GEMMs in fp32 (fp32 workloads; plain VALU FMA, fp32 accumulate).
 //
 // Same grouping and tile scheduling as the bf16 path (routed groups from the
-// permutation, the shared MLP as group N_r over all tokens), with 64-row
-// tiles.  Source: "Shared Expert" (How it works: SwiGLU; Official code: fused
+// permutation, the shared MLP as group N_r over all tokens), with 32-row
+// tiles: at the small batches of the fp32 workloads the tiles cannot fill the
+// chip, and each thread's serial chain of FMAs sets a tile's time, so tiles of
+// half the height give twice the work-groups and half the chain (the tiny
+// layer: gate/up 12.8 against 16.6 us, the layer 0.055 against 0.061 ms;
+// 16-row tiles were no faster).  Source: "Shared Expert" (How it works: SwiGLU; Official code: fused
 // shared MLP of width N_s*f on the full batch).
 #include <algorithm>
 
 #include "common.h"
 
-#define F_BM 64
+#define F_BM 32
+#define F_RM (F_BM / 16)  // rows per thread
 #define F_BN 64
 #define F_BK 16
-#define F_BM_IDX 2  // moe_bm_of(2) == 64
+#define F_BM_IDX 1  // moe_bm_of(1) == 32
 
 struct GemmArgsF {
   const float *A, *A_sh;
@@ -63,7 +68,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgsF a) {
     N = a.N_sh;
   }
   const float *Abase = shared ? a.A_sh : a.A;
-  // loader: 4 A and 4 B elements per thread per k-tile
+  // loader: F_RM A and 4 B elements per thread per k-tile
   const float *ap[4];
   const float *bp[4];
   bool bok[4];
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgsF a) {
     const int c = tid + 256 * q;
     lr[q] = c >> 4;
     lc[q] = c & 15;
-    const int r = min(lr[q], valid - 1);
+    const int r = min(lr[q] % F_BM, valid - 1);
     const int64_t arow = (GATEUP && !shared) ? (int64_t)a.row_token[rb + r] : rb + r;
     ap[q] = Abase + arow * K + lc[q];
     int n;
@@ -92,38 +97,38 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgsF a) {
   int bcol[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) bcol[j] = GATEUP ? ((j >> 1) * 32 + tx * 2 + (j & 1)) : (tx * 4 + j);
-  float acc[4][4] = {};
+  float acc[F_RM][4] = {};
   // the next k-tile's elements are loaded into registers while the current
   // one is multiplied (the same additions in the same order)
   float na[4], nb[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    na[q] = ap[q][0];
+    na[q] = q < F_RM ? ap[q][0] : 0.f;
     nb[q] = bok[q] ? bp[q][0] : 0.f;
   }
   for (int k0 = 0; k0 < K; k0 += F_BK) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      As[lr[q]][lc[q]] = na[q];
+      if (q < F_RM) As[lr[q]][lc[q]] = na[q];
       Bs[lr[q]][lc[q]] = nb[q];
     }
     __syncthreads();
     if (k0 + F_BK < K) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        na[q] = ap[q][k0 + F_BK];
+        na[q] = q < F_RM ? ap[q][k0 + F_BK] : 0.f;
         nb[q] = bok[q] ? bp[q][k0 + F_BK] : 0.f;
       }
     }
 #pragma unroll
     for (int kk = 0; kk < F_BK; ++kk) {
-      float av[4], bv[4];
+      float av[F_RM], bv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = As[ty * 4 + i][kk];
+      for (int i = 0; i < F_RM; ++i) av[i] = As[ty * F_RM + i][kk];
 #pragma unroll
       for (int j = 0; j < 4; ++j) bv[j] = Bs[bcol[j]][kk];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < F_RM; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
     }
@@ -131,8 +136,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgsF a) {
   }
   float *C = shared ? a.C_sh : a.C;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = ty * 4 + i;
+  for (int i = 0; i < F_RM; ++i) {
+    const int row = ty * F_RM + i;
     if (row >= valid) continue;
     if (GATEUP) {
 #pragma unroll
